@@ -1,0 +1,146 @@
+"""Seeded synthetic inputs for attention prefill and paged decode.
+
+This module only draws random numbers and lays out index structures; it holds
+none of the attention arithmetic. Both the HIP path and the CPU oracle consume
+what it returns, so neither depends on the other.
+
+Recipe (the same for every consumer):
+
+* Values: i.i.d. N(0, 1) drawn in fp32 by ``torch.randn`` with a
+  ``torch.Generator`` seeded with ``seed``, then rounded to the element type
+  (bf16 by round-to-nearest-even). Large paged pools may be drawn directly on
+  the GPU with a CUDA generator (``device="cuda"``); that stream differs from
+  the CPU one but is just as fixed by the seed.
+* Prefill draw order: q, k, v.
+* Paged draw order: seq_lens (uniform integers in [lo, hi]), a random
+  permutation of all physical blocks, then q, k_cache, v_cache.
+* Physical pool: sum over sequences of ceil(L_n / 16) blocks plus
+  ``spare_frac`` spare blocks, shuffled; sequence n takes the next
+  ceil(L_n / 16) entries of the permutation as its table row; unused table
+  slots hold -1. With ``poison=True`` the spare blocks and every cache slot
+  past a sequence's length hold NaN, so any read of data the method must not
+  touch shows up in the result.
+"""
+
+import math
+
+import torch
+
+BLOCK_SIZE = 16
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def prefill_inputs(B, Hq, Hkv, T, d, dtype=torch.bfloat16, seed=0, device="cpu"):
+    """q [B,Hq,T,d], k and v [B,Hkv,T,d], i.i.d. N(0,1) rounded to ``dtype``."""
+    g = _gen(seed, device)
+    q = torch.randn(B, Hq, T, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    k = torch.randn(B, Hkv, T, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    v = torch.randn(B, Hkv, T, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    return q, k, v
+
+
+def paged_inputs(num_seqs, Hq, Hkv, d, seq_len_range=None, seq_lens=None, q_lens=None,
+                 dtype=torch.bfloat16, seed=0, spare_frac=0.05, poison=True,
+                 device="cpu", max_blocks_per_seq=None):
+    """A paged batch.
+
+    Either ``seq_len_range=(lo, hi)`` (drawn) or ``seq_lens`` (given) fixes the
+    lengths. ``q_lens`` (default all 1) gives the query tokens per sequence;
+    query_start_loc is their running sum.
+
+    Returns a dict with q [num_tokens,Hq,d], k_cache/v_cache
+    [num_blocks,Hkv,16,d], block_table int32 [num_seqs,max_blocks_per_seq],
+    seq_lens int32, query_start_loc int32 [num_seqs+1], and the host-side
+    bounds max_seq_len, max_query_len, max_blocks_per_seq, num_blocks.
+    """
+    g = _gen(seed, device)
+    if seq_lens is None:
+        lo, hi = seq_len_range
+        lens = torch.randint(lo, hi + 1, (num_seqs,), generator=g, device=device)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int64, device=device)
+    lens_host = [int(x) for x in lens.cpu().tolist()]
+    if q_lens is None:
+        q_lens = [1] * num_seqs
+    q_lens = [int(x) for x in q_lens]
+    nblk = [math.ceil(L / BLOCK_SIZE) for L in lens_host]
+    used = sum(nblk)
+    num_blocks = max(1, used + int(math.ceil(used * spare_frac)))
+    perm = torch.randperm(num_blocks, generator=g, device=device).cpu()
+    mbps = max(1, max(nblk) if nblk else 1)
+    if max_blocks_per_seq is not None:
+        mbps = max(mbps, int(max_blocks_per_seq))
+    table = torch.full((num_seqs, mbps), -1, dtype=torch.int32)
+    off = 0
+    for n, nb in enumerate(nblk):
+        table[n, :nb] = perm[off:off + nb].to(torch.int32)
+        off += nb
+    num_tokens = sum(q_lens)
+    q = torch.randn(num_tokens, Hq, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    k_cache = _randn_big((num_blocks, Hkv, BLOCK_SIZE, d), g, device, dtype)
+    v_cache = _randn_big((num_blocks, Hkv, BLOCK_SIZE, d), g, device, dtype)
+    if poison:
+        spare = perm[off:].to(device)
+        if spare.numel():
+            k_cache[spare] = float("nan")
+            v_cache[spare] = float("nan")
+        for n, L in enumerate(lens_host):
+            if L % BLOCK_SIZE:
+                last = int(table[n, nblk[n] - 1])
+                k_cache[last, :, L % BLOCK_SIZE:, :] = float("nan")
+                v_cache[last, :, L % BLOCK_SIZE:, :] = float("nan")
+    qsl = torch.zeros(num_seqs + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(torch.tensor(q_lens, dtype=torch.int64), 0).to(torch.int32)
+    return {
+        "q": q,
+        "k_cache": k_cache,
+        "v_cache": v_cache,
+        "block_table": table.to(device),
+        "seq_lens": torch.tensor(lens_host, dtype=torch.int32, device=device),
+        "query_start_loc": qsl.to(device),
+        "max_seq_len": max(lens_host) if lens_host else 0,
+        "max_query_len": max(q_lens) if q_lens else 0,
+        "max_blocks_per_seq": mbps,
+        "num_blocks": num_blocks,
+        "q_lens": q_lens,
+        "seq_lens_host": lens_host,
+    }
+
+
+def _randn_big(shape, g, device, dtype):
+    """N(0,1) in ``dtype``, drawn in fp32 chunks so that huge pools fit in memory."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(shape[0], -1)
+    rows_per_chunk = max(1, (1 << 26) // max(1, flat.shape[1]))
+    for r0 in range(0, shape[0], rows_per_chunk):
+        r1 = min(shape[0], r0 + rows_per_chunk)
+        flat[r0:r1] = torch.randn(r1 - r0, flat.shape[1], generator=g, device=device,
+                                  dtype=torch.float32).to(dtype)
+    return out
+
+
+def permute_blocks(batch, seed):
+    """The same logical batch with its physical blocks shuffled again.
+
+    Returns new (k_cache, v_cache, block_table): physical block p moves to
+    position pi[p], and the table is rewritten so that every logical position
+    still names the same values.
+    """
+    g = _gen(seed, "cpu")
+    nb = batch["k_cache"].shape[0]
+    pi = torch.randperm(nb, generator=g)
+    inv = torch.empty_like(pi)
+    inv[pi] = torch.arange(nb)
+    dev = batch["k_cache"].device
+    k_new = torch.empty_like(batch["k_cache"])
+    v_new = torch.empty_like(batch["v_cache"])
+    k_new[pi.to(dev)] = batch["k_cache"]
+    v_new[pi.to(dev)] = batch["v_cache"]
+    t = batch["block_table"].cpu().to(torch.int64)
+    t_new = torch.where(t >= 0, pi[t.clamp(min=0)], t).to(torch.int32)
+    return k_new, v_new, t_new.to(batch["block_table"].device)
