@@ -1,0 +1,162 @@
+/*
+ * attn.h — C ABI of libattn.so: fused scaled-dot-product attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Two operations, as the source pages state the problem:
+ *
+ *  - attn_prefill: causal (or full) attention over contiguous Q, K, V,
+ *    computed block by block so that the T x T score matrix never reaches
+ *    HBM: per block of keys the kernel forms part of the scores, updates the
+ *    running softmax statistics and accumulates the output in on-chip
+ *    memory. ("Fast attention kernels and operator fusion", the-ai.news,
+ *    section "FlashAttention-style attention and paged attention", first
+ *    paragraph.) The result is the naive definition — Q K^T, scaling, causal
+ *    mask, row softmax, product with V ("Hugging Face attention profiling
+ *    guide", aiexpert.news, second paragraph) — up to rounding order.
+ *
+ *  - attn_decode_paged: attention of the batch's new query tokens against a
+ *    paged KV cache of fixed 16-token blocks, every logical position being
+ *    translated through a block table (same page and section, second and
+ *    third paragraphs: fixed-size blocks, a table from logical positions to
+ *    physical blocks, block_size = 16).
+ *
+ * Conventions shared by all entry points
+ *  - Every pointer is caller-owned DEVICE memory (except where noted). The
+ *    library never allocates, frees or keeps a pointer after returning.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without waiting. There is no host synchronisation
+ *    and no device-to-host read, and launch shapes depend on host arguments
+ *    only, so the calls may be captured in a HIP graph (the pages' reason for
+ *    graph replay: fixed shapes and fixed addresses, "Fast attention kernels
+ *    and operator fusion", section "Fusion and CUDA Graphs with
+ *    torch.compile").
+ *  - Arguments are validated on the host BEFORE any HIP call. An invalid or
+ *    unsupported request returns a negative status and launches nothing: the
+ *    library never falls back to another algorithm (the pages warn that a
+ *    silent fallback to an unfused path is the hardest risk to see,
+ *    "Hugging Face attention profiling guide", last paragraph).
+ *  - A launch failure reported by the HIP runtime returns ATTN_ERR_LAUNCH.
+ *  - bf16 is IEEE bfloat16 (the upper 16 bits of an fp32). Products are
+ *    accumulated in fp32; the softmax weights are rounded to bf16
+ *    (round-to-nearest-even) before the product with V; outputs are rounded
+ *    to the output type at the end.
+ *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *  - `scale` multiplies the scores before the softmax; it must be finite and
+ *    > 0 (use 1/sqrt(d) for the usual scaling).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  ATTN_ERR_UNSUPPORTED = -3, /* valid request outside the supported set */
+  ATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  ATTN_ERR_LAUNCH = -6       /* the HIP runtime rejected a launch */
+};
+
+/*
+ * attn_prefill — o = softmax(scale * q k^T [+ causal mask]) v, per (batch,
+ * query head).
+ *
+ * Layout (row-major, contiguous, element type `dtype`):
+ *   q, o : [B][Hq][T][d]
+ *   k, v : [B][Hkv][T][d]
+ *   lse  : [B][Hq][T] fp32, optional (NULL = not written):
+ *          lse = log(sum_j exp(scale * q.k_j)) over the keys the row sees.
+ * causal = 1: query i sees keys 0..i; causal = 0: all T keys.
+ * Supported: d in {64, 128}; dtype ATTN_BF16 (MFMA path) or ATTN_F32;
+ * Hq % Hkv == 0; B, Hq, Hkv, T >= 1; q, k, v, o 16-byte aligned; lse 4-byte
+ * aligned. q/k/v must not overlap o or lse.
+ * Returns ATTN_OK or a negative status; on error nothing is launched.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 int B, int Hq, int Hkv, int T, int d, float scale, int causal,
+                 attn_dtype dtype, float* lse, void* stream);
+
+/*
+ * attn_decode_paged_partition_size — the KV partition length (tokens) that
+ * attn_decode_paged uses for these arguments when it is passed
+ * partition_size = 0. A pure function of its arguments. Returns 0 if the
+ * arguments are out of range.
+ */
+int attn_decode_paged_partition_size(int num_seqs, int Hkv, int max_seq_len);
+
+/*
+ * attn_decode_paged_workspace_size — bytes of device workspace that
+ * attn_decode_paged needs for the same arguments (partition_size as passed
+ * to attn_decode_paged, 0 = automatic). Returns 0 if the arguments are out
+ * of range. The workspace holds the fp32 split-KV partial results; its
+ * contents need no initialisation and are garbage after the call.
+ */
+size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
+                                        int max_seq_len, int partition_size);
+
+/*
+ * attn_decode_paged — attention of the batch's query tokens against a paged
+ * KV cache.
+ *
+ * Layout:
+ *   q, o         : [num_tokens][Hq][d] bf16, token-major
+ *   k_cache,
+ *   v_cache      : [num_blocks][Hkv][block_size][d] bf16 (one (block, head)
+ *                  is block_size * d contiguous elements)
+ *   block_table  : int32 [num_seqs][max_blocks_per_seq]; entry b of row n is
+ *                  the physical block holding logical positions
+ *                  16b .. 16b+15 of sequence n
+ *   seq_lens     : int32 [num_seqs]; L_n = number of cached positions of
+ *                  sequence n, including the K/V of its current query tokens
+ *   query_start_loc : int32 [num_seqs + 1] or NULL. Sequence n owns query
+ *                  rows qsl[n] .. qsl[n+1]-1 of q/o (q_len_n of them), which
+ *                  are its LAST q_len_n positions L_n - q_len_n .. L_n - 1;
+ *                  the query at position t sees keys 0..t. NULL means one
+ *                  query per sequence (row n) that sees all L_n keys.
+ *   lse          : [num_tokens][Hq] fp32, optional (NULL = not written).
+ *   workspace    : device memory of at least
+ *                  attn_decode_paged_workspace_size(...) bytes (may be NULL
+ *                  if that size is 0), 256-byte aligned.
+ * Host-side bounds (the caller knows them; nothing is read back):
+ *   max_seq_len   >= every L_n;  max_query_len >= every q_len_n (1 when
+ *   query_start_loc is NULL);  max_blocks_per_seq >= ceil(max_seq_len/16).
+ * Sequences with q_len_n == 1 take the split-KV decode path (partitions of
+ * partition_size tokens, 0 = automatic, else a positive multiple of 16, then
+ * a log-sum-exp merge); sequences with q_len_n >= 2 take the tiled prefill
+ * path reading K/V tiles through the block table.
+ * Preconditions not checked on the device: table entries for logical blocks
+ * < ceil(L_n/16) lie in [0, num_blocks); 0 <= L_n <= max_seq_len;
+ * q_len_n <= L_n; query_start_loc is non-decreasing with qsl[num_seqs] <=
+ * num_tokens. Table entries past ceil(L_n/16) are never read and may hold
+ * anything (e.g. -1); cache slots at positions >= L_n are never read. A row
+ * that sees no key (L_n = 0) gets o = 0 and lse = -inf.
+ * Supported: d in {64, 128}; dtype ATTN_BF16; block_size == 16;
+ * Hq % Hkv == 0 and Hq / Hkv <= 16.
+ * Returns ATTN_OK or a negative status; on error nothing is launched.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, void* o,
+                      int num_seqs, int num_tokens, int Hq, int Hkv, int d,
+                      int block_size, int max_blocks_per_seq, int max_seq_len,
+                      int max_query_len, int64_t num_blocks, float scale,
+                      attn_dtype dtype, int partition_size, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_status_string — static, human-readable text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -118,12 +118,16 @@ def gather_paged_kv(cache, block_table_row, seq_len, block_size=16):
     cache: [num_blocks, Hkv, block_size, d]. Logical position p lives in
     physical block block_table_row[p // block_size], slot p % block_size.
     """
-    cache = _as_f64(cache)
     table = np.asarray(block_table_row, dtype=np.int64)
     p = np.arange(int(seq_len))
     phys = table[p // block_size]
     slot = p % block_size
-    return cache[phys, :, slot, :]  # [L, Hkv, d]
+    if hasattr(cache, "detach"):  # torch tensor: pick the rows first, then convert them
+        import torch  # local import: only needed for torch inputs
+
+        rows = cache.detach()[torch.from_numpy(phys), :, torch.from_numpy(slot), :]
+        return _as_f64(rows)  # [L, Hkv, d]
+    return np.asarray(cache)[phys, :, slot, :].astype(np.float64)  # [L, Hkv, d]
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale,

@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad requests on the host before any HIP call (so these run without a
+GPU; no test here launches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_tiled_amd as attn
+from transformer_attention_tiled_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+
+# Fake device addresses: never dereferenced, because validation fails first.
+P = 0x100000
+P2 = 0x900000
+P3 = 0x1100000
+P4 = 0x1900000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return attn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_prefill", "attn_decode_paged", "attn_status_string",
+            "attn_decode_paged_workspace_size", "attn_decode_paged_partition_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH):
+        s = attn.status_string(code)
+        assert s and s != "unknown status"
+    assert attn.status_string(12345) == "unknown status"
+
+
+def prefill(lib, q=P, k=P2, v=P3, o=P4, B=1, Hq=2, Hkv=2, T=16, d=64, scale=0.125, causal=1,
+            dtype=BF16, lse=None):
+    return lib.attn_prefill(q, k, v, o, B, Hq, Hkv, T, d, ctypes.c_float(scale), causal, dtype,
+                            lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(Hq=6, Hkv=4), SHAPE), (dict(causal=2), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(scale=0.0), UNSUP), (dict(scale=-1.0), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(scale=float("inf")), UNSUP),
+    (dict(q=P + 8), ALIGN), (dict(o=P4 + 4), ALIGN), (dict(lse=P + 2), ALIGN),
+    (dict(o=P), SHAPE),            # output overlaps q
+    (dict(lse=P4 + 64), SHAPE),    # lse overlaps o
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def decode(lib, q=P, kc=P2, vc=P3, table=P4, seq_lens=P4 + 0x10000, qsl=None, o=P4 + 0x20000,
+           num_seqs=4, num_tokens=4, Hq=8, Hkv=2, d=128, block_size=16, mbps=8, max_seq_len=128,
+           max_query_len=1, num_blocks=64, scale=0.1, dtype=BF16, partition_size=0, lse=None,
+           ws=0x4000000, ws_bytes=1 << 30):
+    return lib.attn_decode_paged(q, kc, vc, table, seq_lens, qsl, o, num_seqs, num_tokens, Hq,
+                                 Hkv, d, block_size, mbps, max_seq_len, max_query_len, num_blocks,
+                                 ctypes.c_float(scale), dtype, partition_size, lse, ws, ws_bytes,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(table=None), NULL),
+    (dict(seq_lens=None), NULL), (dict(o=None), NULL),
+    (dict(dtype=F32), UNSUP), (dict(d=80), UNSUP), (dict(block_size=32), UNSUP),
+    (dict(Hq=34, Hkv=2), UNSUP), (dict(scale=0.0), UNSUP),
+    (dict(num_seqs=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(max_seq_len=0), SHAPE),
+    (dict(mbps=7), SHAPE), (dict(num_blocks=0), SHAPE), (dict(max_query_len=2), SHAPE),
+    (dict(num_tokens=3), SHAPE), (dict(partition_size=8), SHAPE), (dict(partition_size=-16), SHAPE),
+    (dict(max_query_len=200, qsl=P4 + 0x30000, num_tokens=300), SHAPE),
+    (dict(q=P + 4), ALIGN), (dict(table=P4 + 2), ALIGN), (dict(ws=0x4000000 + 16), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS),
+    (dict(o=P), SHAPE),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_workspace_size_and_partition_policy():
+    # pure host functions
+    P_auto = attn.decode_paged_partition_size(64, 2, 4096)
+    assert P_auto > 0 and P_auto % 16 == 0
+    assert attn.decode_paged_partition_size(0, 2, 4096) == 0
+    ws = attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 256)
+    parts = 4096 // 256
+    rows = 64 * 12 * parts
+    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert ws == expect
+    assert attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 8) == 0    # not a multiple of 16
+    assert attn.decode_paged_workspace_size(64, 12, 2, 96, 4096, 0) == 0     # d unsupported
+    # automatic partition length: the workspace query and the launch agree
+    assert (attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 0)
+            == attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, P_auto))
+
+
+def test_binding_raises_attn_error_with_code(lib):
+    e = _binding.AttnError(SHAPE, "attn_prefill")
+    assert e.status == SHAPE and "ATTN_ERR_SHAPE" in str(e)

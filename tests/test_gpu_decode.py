@@ -1,0 +1,131 @@
+"""GPU parity of attn_decode_paged (one query per sequence) against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_tiled_amd as attn
+from transformer_attention_tiled_amd import inputs
+from parity import assert_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def to_dev(b):
+    return {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in b.items()}
+
+
+def run(b, partition_size=0, with_qsl=False, want_lse=True):
+    d = to_dev(b)
+    lse = torch.full(tuple(d["q"].shape[:2]), float("nan"), device=DEV) if want_lse else None
+    o = attn.decode_paged(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                          max_seq_len=max(1, b["max_seq_len"]), max_query_len=b["max_query_len"],
+                          query_start_loc=d["query_start_loc"] if with_qsl else None,
+                          partition_size=partition_size, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def reference(b):
+    return oracle.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+                               b["seq_lens"], 1.0 / math.sqrt(b["q"].shape[-1]))
+
+
+def check(b, partition_size=0, with_qsl=False, what=""):
+    o, lse = run(b, partition_size, with_qsl)
+    ro, rl = reference(b)
+    assert_close(o, ro, torch.bfloat16, what)
+    assert_lse_close(lse, rl, what)
+    return o, lse
+
+
+def test_config_decode_64_seqs():
+    # 64 sequences, Hq=12, Hkv=2, d=128, lengths uniform in [256, 4096]
+    print("[decode] 64 seqs Hq=12 Hkv=2", flush=True)
+    b = inputs.paged_inputs(64, 12, 2, 128, seq_len_range=(256, 4096), seed=4)
+    check(b, what="64 seqs")
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1000]
+
+
+@pytest.mark.parametrize("P", [0, 16, 32, 256, 512, 4096])
+def test_edge_lengths_all_partition_sizes(P):
+    print(f"[decode] edge lengths P={P}", flush=True)
+    b = inputs.paged_inputs(len(EDGE_LENS), 8, 2, 128, seq_lens=EDGE_LENS, seed=40 + P)
+    check(b, partition_size=P, what=f"P={P}")
+
+
+@pytest.mark.parametrize("G", [1, 4, 6, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_sizes(G, d):
+    print(f"[decode] G={G} d={d}", flush=True)
+    b = inputs.paged_inputs(7, 2 * G, 2, d, seq_len_range=(1, 700), seed=50 + G + d)
+    check(b, what=f"G={G} d={d}")
+
+
+def test_partition_size_invariance():
+    b = inputs.paged_inputs(9, 12, 2, 128, seq_len_range=(1, 2000), seed=60)
+    outs = [run(b, P) for P in (16, 32, 256, 512, 2048)]
+    base_o, base_l = outs[-1]  # one partition per sequence: the unsplit case
+    for o, l in outs[:-1]:
+        # The merge identity is exact, but each partition rounds its weights
+        # P to bf16 against its own running max, so splits differ by that
+        # rounding (relative 2^-9 per weight), far below the oracle bound.
+        diff = (o.float() - base_o.float()).abs()
+        assert diff.max().item() <= 2e-3 and diff.mean().item() <= 2e-4
+        # lse sums unrounded fp32 weights: agreement to fp32 rounding
+        assert torch.allclose(l, base_l, atol=1e-5, rtol=0)
+
+
+def test_block_permutation_is_bitwise_invisible():
+    b = inputs.paged_inputs(12, 8, 2, 128, seq_len_range=(1, 900), seed=61)
+    o1, l1 = run(b)
+    k2, v2, t2 = inputs.permute_blocks(b, seed=62)
+    b2 = dict(b, k_cache=k2, v_cache=v2, block_table=t2)
+    o2, l2 = run(b2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_poisoned_storage_and_padded_table():
+    # spare blocks and tail slots hold NaN; table slots past the length are -1
+    b = inputs.paged_inputs(6, 4, 1, 128, seq_lens=[3, 17, 33, 100, 250, 16], seed=63,
+                            spare_frac=0.5, max_blocks_per_seq=40)
+    assert torch.isnan(b["k_cache"]).any() and (b["block_table"] == -1).any()
+    check(b, what="poisoned")
+
+
+def test_empty_sequence():
+    b = inputs.paged_inputs(3, 4, 2, 128, seq_lens=[0, 5, 40], seed=64)
+    o, lse = run(b)
+    assert torch.equal(o[0].float(), torch.zeros_like(o[0].float()))
+    assert torch.isinf(lse[0]).all() and (lse[0] < 0).all()
+    ro, _ = reference(b)
+    assert_close(o[1:], ro[1:], torch.bfloat16, "empty neighbours")
+
+
+def test_deterministic():
+    b = inputs.paged_inputs(16, 12, 2, 128, seq_len_range=(1, 3000), seed=65)
+    o1, l1 = run(b)
+    o2, l2 = run(b)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_query_start_loc_all_ones_same_as_null():
+    b = inputs.paged_inputs(10, 8, 2, 128, seq_len_range=(1, 600), seed=66)
+    o1, l1 = run(b)
+    o2, l2 = run(b, with_qsl=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workspace_too_small_is_an_error():
+    b = to_dev(inputs.paged_inputs(4, 8, 2, 128, seq_len_range=(1, 100), seed=67))
+    ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(attn.AttnError) as e:
+        attn.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                          max_seq_len=b["max_seq_len"], workspace=ws)
+    assert e.value.status == -5

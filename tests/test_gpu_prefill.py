@@ -1,0 +1,135 @@
+"""GPU parity of attn_prefill against the CPU oracle (through the C ABI)."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_tiled_amd as attn
+from transformer_attention_tiled_amd import inputs
+from parity import assert_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(q, k, v, causal=True, scale=None, want_lse=True):
+    B, Hq, T, d = q.shape
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lse = torch.full((B, Hq, T), float("nan"), device=DEV) if want_lse else None
+    o = attn.prefill(qd, kd, vd, causal=causal, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def case(B, Hq, Hkv, T, d, dtype, causal, seed):
+    print(f"[prefill] B={B} Hq={Hq} Hkv={Hkv} T={T} d={d} {dtype} causal={causal} seed={seed}",
+          flush=True)
+    sys.stdout.flush()
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, T, d, dtype, seed=seed)
+    o, lse = run(q, k, v, causal)
+    ref_o, ref_lse = oracle.prefill(q, k, v, 1.0 / math.sqrt(d), causal=causal)
+    assert_close(o, ref_o, dtype, f"T={T} d={d}")
+    assert_lse_close(lse, ref_lse, f"T={T} d={d}")
+
+
+def test_config_fp32_small():
+    # B=1, Hq=Hkv=2, T=128, d=64, fp32, causal, scale 1/sqrt(d)
+    case(1, 2, 2, 128, 64, torch.float32, True, seed=1)
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 129, 200])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_ragged(T, d):
+    case(2, 4, 2, T, d, torch.float32, True, seed=11 + T)
+    case(1, 2, 1, T, d, torch.float32, False, seed=12 + T)
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 300])
+def test_bf16_ragged_d128(T):
+    case(2, 4, 2, T, 128, torch.bfloat16, True, seed=100 + T)
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 129, 257])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_bf16_gqa_d64(T, G):
+    case(1, 4, 4 // G, T, 64, torch.bfloat16, True, seed=200 + T + G)
+
+
+@pytest.mark.parametrize("T", [1, 40, 128, 333])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_non_causal(T, d):
+    case(2, 2, 1, T, d, torch.bfloat16, False, seed=300 + T)
+
+
+def test_config_bf16_b4_t2048():
+    # B=4, Hq=Hkv=16, T=2048, d=128: full oracle
+    case(4, 16, 16, 2048, 128, torch.bfloat16, True, seed=2)
+
+
+def test_config_bf16_gqa_t16384_sampled():
+    # B=1, Hq=32, Hkv=8, T=16384, d=128: heads at group boundaries, sampled rows
+    print("[prefill] long GQA config T=16384", flush=True)
+    q, k, v = inputs.prefill_inputs(1, 32, 8, 16384, 128, torch.bfloat16, seed=3)
+    o, lse = run(q, k, v, True)
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 4095, 8191, 8192, 16256, 16383] +
+                      rng.integers(0, 16384, 36).tolist()))
+    heads = [0, 3, 4, 31]
+    ref_o, ref_lse = oracle.prefill(q, k, v, 1.0 / math.sqrt(128), causal=True, rows=rows,
+                                    heads=heads)
+    got = o[:, heads][:, :, rows]
+    assert_close(got, ref_o[:, heads], torch.bfloat16, "T=16384 sampled")
+    assert_lse_close(lse[:, heads][:, :, rows], ref_lse[:, heads], "T=16384 sampled")
+    assert torch.isfinite(o).all()
+
+
+def test_causality_is_exact():
+    # Rows <= i are bitwise unchanged when everything after position i changes.
+    q, k, v = inputs.prefill_inputs(1, 4, 2, 300, 128, torch.bfloat16, seed=21)
+    o1, _ = run(q, k, v, True, want_lse=False)
+    for i in (0, 63, 64, 150, 298):
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()
+        q2[:, :, i + 1:] = q2[:, :, i + 1:] * 3 + 1
+        k2[:, :, i + 1:] = -k2[:, :, i + 1:] * 5
+        v2[:, :, i + 1:] = v2[:, :, i + 1:] * 7 - 2
+        o2, _ = run(q2, k2, v2, True, want_lse=False)
+        assert torch.equal(o1[:, :, :i + 1], o2[:, :, :i + 1]), f"row {i}"
+
+
+def test_deterministic():
+    q, k, v = inputs.prefill_inputs(2, 8, 2, 500, 128, torch.bfloat16, seed=22)
+    o1, l1 = run(q, k, v, True)
+    o2, l2 = run(q, k, v, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_closed_form_zero_query():
+    # q = 0: o_i = mean(v_0..v_i); the kernel must reproduce it within tolerance
+    _, k, v = inputs.prefill_inputs(1, 2, 2, 257, 128, torch.bfloat16, seed=23)
+    q = torch.zeros(1, 2, 257, 128, dtype=torch.bfloat16)
+    o, lse = run(q, k, v, True)
+    vv = v.double().numpy()
+    expect = np.cumsum(vv, axis=2) / np.arange(1, 258)[None, None, :, None]
+    assert_close(o, expect, torch.bfloat16, "q=0")
+    np.testing.assert_allclose(lse.cpu().double().numpy()[0, 0], np.log(np.arange(1, 258)),
+                               atol=1e-4, rtol=0)
+
+
+def test_constant_v():
+    q, k, _ = inputs.prefill_inputs(1, 2, 1, 190, 64, torch.bfloat16, seed=24)
+    row = torch.randn(64, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    v = row.expand(1, 1, 190, 64).contiguous()
+    o, _ = run(q, k, v, True, want_lse=False)
+    expect = np.broadcast_to(row.double().numpy(), (1, 2, 190, 64))
+    assert_close(o, expect, torch.bfloat16, "constant v")
+
+
+def test_rejects_unsupported_without_fallback():
+    q, k, v = inputs.prefill_inputs(1, 2, 2, 16, 96, torch.bfloat16, seed=25)
+    with pytest.raises(attn.AttnError) as e:
+        run(q, k, v, True)
+    assert e.value.status == -3

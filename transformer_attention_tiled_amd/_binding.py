@@ -1,0 +1,166 @@
+"""ctypes binding of libattn.so (the C ABI declared in include/attn.h).
+
+Argument marshalling only: tensors become raw device pointers, the current
+HIP stream is passed through, and a non-zero status becomes ``AttnError``.
+No computation happens here, and there is no fallback of any kind: if the
+library cannot be loaded, every entry point raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn.so"
+_lib = None
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+_STATUS_NAMES = {
+    0: "ATTN_OK",
+    -1: "ATTN_ERR_NULL",
+    -2: "ATTN_ERR_SHAPE",
+    -3: "ATTN_ERR_UNSUPPORTED",
+    -4: "ATTN_ERR_ALIGN",
+    -5: "ATTN_ERR_WORKSPACE",
+    -6: "ATTN_ERR_LAUNCH",
+}
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a negative status."""
+
+    def __init__(self, status, where):
+        self.status = status
+        self.name = _STATUS_NAMES.get(status, str(status))
+        try:
+            text = status_string(status)
+        except Exception:  # library not loadable: keep the code only
+            text = ""
+        super().__init__(f"{where}: {self.name} ({status}) {text}")
+
+
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libattn.so (once). Raises if it is missing or broken."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.attn_prefill.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int, c_int, c_int, c_int, c_int, c_float, c_int,
+                                 c_int, c_void_p, c_void_p]
+    lib.attn_prefill.restype = c_int
+    lib.attn_decode_paged_partition_size.argtypes = [c_int, c_int, c_int]
+    lib.attn_decode_paged_partition_size.restype = c_int
+    lib.attn_decode_paged_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.attn_decode_paged_workspace_size.restype = c_size_t
+    lib.attn_decode_paged.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p,
+                                      c_int, c_int, c_int, c_int, c_int,
+                                      c_int, c_int, c_int, c_int, ctypes.c_int64, c_float,
+                                      c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.attn_decode_paged.restype = c_int
+    lib.attn_status_string.argtypes = [c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return ATTN_BF16
+    if dt == torch.float32:
+        return ATTN_F32
+    return -1  # the library rejects it with ATTN_ERR_UNSUPPORTED
+
+
+def _check(status, where):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def prefill(q, k, v, o=None, *, scale=None, causal=True, lse=None):
+    """attn_prefill on contiguous tensors q [B,Hq,T,d], k/v [B,Hkv,T,d].
+
+    Returns o (allocated like q when not given). ``lse`` (fp32 [B,Hq,T]) is
+    filled when given.
+    """
+    lib = load_library()
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    status = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, T, d,
+                              float(scale), int(bool(causal)), _dtype_code(q.dtype), _ptr(lse),
+                              _stream(q.device))
+    _check(status, "attn_prefill")
+    return o
+
+
+def decode_paged_partition_size(num_seqs, Hkv, max_seq_len):
+    return int(load_library().attn_decode_paged_partition_size(num_seqs, Hkv, max_seq_len))
+
+
+def decode_paged_workspace_size(num_seqs, Hq, Hkv, d, max_seq_len, partition_size=0):
+    return int(load_library().attn_decode_paged_workspace_size(num_seqs, Hq, Hkv, d, max_seq_len,
+                                                               partition_size))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, max_query_len=1,
+                 query_start_loc=None, o=None, scale=None, partition_size=0, lse=None,
+                 workspace=None):
+    """attn_decode_paged. q [num_tokens,Hq,d]; caches [num_blocks,Hkv,16,d].
+
+    ``max_seq_len`` / ``max_query_len`` are host-side bounds the caller knows
+    (nothing is read back from the device). A workspace is allocated when not
+    given. Returns o.
+    """
+    lib = load_library()
+    num_tokens, Hq, d = q.shape
+    num_blocks, Hkv, block_size, _ = k_cache.shape
+    num_seqs = seq_lens.shape[0]
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = decode_paged_workspace_size(num_seqs, Hq, Hkv, d, max_seq_len, partition_size)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib.attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(query_start_loc), _ptr(o), num_seqs, num_tokens, Hq, Hkv, d, block_size,
+        block_table.shape[1], int(max_seq_len), int(max_query_len), num_blocks, float(scale),
+        _dtype_code(q.dtype), int(partition_size), _ptr(lse), _ptr(workspace), ws_have,
+        _stream(q.device))
+    _check(status, "attn_decode_paged")
+    return o

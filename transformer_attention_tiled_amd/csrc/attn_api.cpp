@@ -1,0 +1,176 @@
+// C ABI of libattn.so (declared in include/attn.h): host-side validation,
+// then launch on the caller's stream. Every check runs before the first HIP
+// call, so an invalid request launches nothing and touches no device state;
+// no request is ever re-routed to another algorithm (the pages name a silent
+// fallback to an unfused path as the integration risk that only a profiler
+// reveals: "Hugging Face attention profiling guide", aiexpert.news, last
+// paragraph).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (a == nullptr || b == nullptr) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Bytes of the split-KV workspace: partial outputs, then partial lse.
+struct WsLayout {
+  int partition_size = 0;
+  int max_parts = 0;
+  size_t o_bytes = 0;
+  size_t total = 0;
+};
+
+bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partition_size,
+               WsLayout* w) {
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || !supported_d(d)) return false;
+  if (partition_size < 0 || partition_size % attn::kBlockSize != 0) return false;
+  const int P = partition_size > 0 ? partition_size
+                                   : attn::decode_partition_size(num_seqs, Hkv, max_seq_len);
+  if (P <= 0) return false;
+  const int64_t parts = ((int64_t)max_seq_len + P - 1) / P;
+  const int64_t rows = (int64_t)num_seqs * Hq * parts;
+  const int64_t o_bytes = (rows * d * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  w->partition_size = P;
+  w->max_parts = (int)parts;
+  w->o_bytes = (size_t)o_bytes;
+  w->total = (size_t)(o_bytes + l_bytes);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case ATTN_ERR_UNSUPPORTED: return "request outside the supported set (d, dtype, block size, GQA ratio, scale)";
+    case ATTN_ERR_ALIGN: return "a pointer is not aligned as required";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                 int T, int d, float scale, int causal, attn_dtype dtype, float* lse,
+                 void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (!supported_d(d) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  const int64_t esize = dtype == ATTN_BF16 ? 2 : 4;
+  const int64_t qbytes = (int64_t)B * Hq * T * d * esize;
+  const int64_t kvbytes = (int64_t)B * Hkv * T * d * esize;
+  const int64_t lbytes = (int64_t)B * Hq * T * 4;
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kvbytes) ||
+      overlap(o, qbytes, v, kvbytes) || overlap(lse, lbytes, q, qbytes) ||
+      overlap(lse, lbytes, k, kvbytes) || overlap(lse, lbytes, v, kvbytes) ||
+      overlap(lse, lbytes, o, qbytes))
+    return ATTN_ERR_SHAPE;
+  // query tiles of 64 (fp32) or 128 (bf16) rows, all in one grid dimension
+  if ((int64_t)(T + 63) / 64 * B * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
+
+  attn::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.d = d;
+  a.scale = scale; a.causal = causal;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
+                                          : attn::launch_prefill_f32(a, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode_paged_partition_size(int num_seqs, int Hkv, int max_seq_len) {
+  return attn::decode_partition_size(num_seqs, Hkv, max_seq_len);
+}
+
+size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d, int max_seq_len,
+                                        int partition_size) {
+  WsLayout w;
+  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return 0;
+  return w.total;
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, void* o, int num_seqs, int num_tokens,
+                      int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                      int max_seq_len, int max_query_len, int64_t num_blocks, float scale,
+                      attn_dtype dtype, int partition_size, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || o == nullptr)
+    return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || num_tokens < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!supported_d(d) || block_size != attn::kBlockSize || Hq / Hkv > 16 || !good_scale(scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (max_seq_len < 1 || num_blocks < 1 || max_query_len < 1 || max_query_len > max_seq_len ||
+      max_query_len > num_tokens)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq < ((int64_t)max_seq_len + attn::kBlockSize - 1) / attn::kBlockSize)
+    return ATTN_ERR_SHAPE;
+  if (query_start_loc == nullptr && (max_query_len != 1 || num_tokens < num_seqs))
+    return ATTN_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % attn::kBlockSize != 0) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4) ||
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return ATTN_ERR_ALIGN;
+  const int64_t qbytes = (int64_t)num_tokens * Hq * d * 2;
+  const int64_t cbytes = num_blocks * Hkv * attn::kBlockSize * d * 2;
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_cache, cbytes) ||
+      overlap(o, qbytes, v_cache, cbytes) || overlap(lse, (int64_t)num_tokens * Hq * 4, o, qbytes))
+    return ATTN_ERR_SHAPE;
+  WsLayout w;
+  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
+  if (workspace == nullptr || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
+  if ((int64_t)w.max_parts * Hkv * num_seqs > kMaxGrid) return ATTN_ERR_SHAPE;
+  const int64_t n_qt = ((int64_t)max_query_len + 127) / 128;
+  if (n_qt * num_seqs * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
+
+  attn::PagedArgs a;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.qsl = query_start_loc;
+  a.o = o; a.lse = lse;
+  a.num_seqs = num_seqs; a.num_tokens = num_tokens; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+  a.max_blocks_per_seq = max_blocks_per_seq; a.max_seq_len = max_seq_len;
+  a.max_query_len = max_query_len; a.num_blocks = num_blocks; a.scale = scale;
+  a.partition_size = w.partition_size; a.max_parts = w.max_parts;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_query_len >= 2) {
+    if (attn::launch_paged_prefill_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  if (attn::launch_paged_decode_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return ATTN_OK;
+}
+
+}  // extern "C"

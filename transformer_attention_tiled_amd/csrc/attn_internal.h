@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (attn_api.cpp) and the kernel
+// launchers. Arguments reaching a launcher have been validated already.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Contiguous prefill: q,o [B][Hq][T][d], k,v [B][Hkv][T][d].
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // [B][Hq][T] or nullptr
+  int B, Hq, Hkv, T, d;
+  float scale;
+  int causal;
+};
+
+// Paged batch: q,o [num_tokens][Hq][d]; caches [num_blocks][Hkv][16][d].
+struct PagedArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;  // [num_seqs][max_blocks_per_seq]
+  const int32_t* seq_lens;     // [num_seqs]
+  const int32_t* qsl;          // [num_seqs + 1] or nullptr (one query per sequence)
+  void* o;
+  float* lse;  // [num_tokens][Hq] or nullptr
+  int num_seqs, num_tokens, Hq, Hkv, d;
+  int max_blocks_per_seq, max_seq_len, max_query_len;
+  int64_t num_blocks;
+  float scale;
+  int partition_size;  // resolved (> 0, multiple of 16)
+  int max_parts;       // ceil(max_seq_len / partition_size)
+  float* ws_o;         // split-KV partial outputs [num_seqs][Hq][max_parts][d]
+  float* ws_lse;       // split-KV partial log2-sum-exp [num_seqs][Hq][max_parts]
+};
+
+constexpr int kBlockSize = 16;
+
+// Host-side policy shared by the workspace query and the launch.
+int decode_partition_size(int num_seqs, int Hkv, int max_seq_len);
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s);  // q_len >= 2 sequences
+hipError_t launch_paged_decode_bf16(const PagedArgs& a, hipStream_t s);   // q_len == 1 sequences
+
+}  // namespace attn
