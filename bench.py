@@ -1,0 +1,328 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = one pass over the whole path on one batch of synthetic input:
+  * causal prefill, bf16, B=1, Hq=32, Hkv=8 (GQA 4), T=16384, d=128
+    (attn_prefill), and
+  * paged decode, bf16, 64 sequences x 1 query, Hq=12, Hkv=2, d=128,
+    block 16, lengths uniform in [256, 4096] (attn_decode_paged).
+Inputs are resident in HBM before the timed region. The decode batch cycles
+through 8 independently drawn KV pools (about 1.2 GB), so that the 256 MB
+last-level cache cannot serve it from a previous step.
+
+Printed: one JSON line. ``value`` is the prefill throughput in TFLOP/s
+(algorithmic causal FLOPs 4*B*Hq*d*T(T+1)/2 over the prefill call's time,
+HIP events on its stream); ``decode`` carries the decode HBM throughput
+(algorithmic bytes: every valid K/V element once, q, o, used table entries
+and lengths, over the decode call's time). ``roofline`` is for the prefill
+kernel against the dense bf16 MFMA peak; ``roofline_decode`` for the decode
+call (split kernel + merge kernel) against the HBM peak. ``cpu_baseline`` is
+the CPU oracle timed on this host on half of the prefill's query heads.
+
+Other workloads (parity configurations, the mixed paged batch) can be timed
+with --workload; only the default is the headline line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import transformer_attention_tiled_amd as attn  # noqa: E402
+from transformer_attention_tiled_amd import inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, MI355X
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal prefill TFLOP/s + paged-decode HBM GB/s on 1 MI355X (% of roofline)"
+ROTATE = 8
+
+
+def causal_flops(B, Hq, T, d):
+    return 4.0 * B * Hq * d * T * (T + 1) / 2
+
+
+def decode_bytes(b, Hq, Hkv, d):
+    lens = b["seq_lens_host"]
+    kv = sum(lens) * Hkv * d * 2 * 2              # each valid K and V element once (bf16)
+    qo = len(lens) * Hq * d * 2 * 2               # q in, o out
+    table = sum(math.ceil(L / 16) for L in lens) * 4 + len(lens) * 4
+    return kv + qo + table
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(torch.cuda.current_stream())
+        return e
+
+    def stop(self, e0):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(torch.cuda.current_stream())
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def make_prefill(cfg, dev):
+    B, Hq, Hkv, T, d, dtype, seed = cfg
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, T, d, dtype, seed=seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    return dict(cpu=(q, k, v), q=qd, k=kd, v=vd, o=o, B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, dtype=dtype)
+
+
+def run_prefill(p):
+    attn.prefill(p["q"], p["k"], p["v"], p["o"], causal=True)
+
+
+def make_decode_sets(n_sets, num_seqs, Hq, Hkv, d, lo, hi, seed, dev, q_lens=None, gen_dev="cpu"):
+    sets = []
+    for r in range(n_sets):
+        b = inputs.paged_inputs(num_seqs, Hq, Hkv, d, seq_len_range=(lo, hi), q_lens=q_lens,
+                                seed=seed + 1000 * r, device=gen_dev)
+        bd = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in b.items()}
+        bd["o"] = torch.empty_like(bd["q"])
+        bd["ws"] = torch.empty(max(1, attn.decode_paged_workspace_size(
+            num_seqs, Hq, Hkv, d, b["max_seq_len"])), dtype=torch.uint8, device=dev)
+        bd["cpu"] = b if r == 0 else None
+        sets.append(bd)
+    return sets
+
+
+def run_decode(bd, with_qsl=False):
+    attn.decode_paged(bd["q"], bd["k_cache"], bd["v_cache"], bd["block_table"], bd["seq_lens"],
+                      max_seq_len=bd["max_seq_len"], max_query_len=bd["max_query_len"],
+                      query_start_loc=bd["query_start_loc"] if with_qsl else None,
+                      o=bd["o"], workspace=bd["ws"])
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_prefill(p, heads=(0,)):
+    """Time the oracle on whole query heads of the prefill; also return the
+    parity of the GPU output on those heads."""
+    import oracle
+
+    q, k, v = p["cpu"]
+    t0 = time.perf_counter()
+    ref, _ = oracle.prefill(q, k, v, 1.0 / math.sqrt(p["d"]), causal=True, heads=list(heads))
+    dt = time.perf_counter() - t0
+    flops = causal_flops(p["B"], len(heads), p["T"], p["d"])
+    got = p["o"].cpu().double().numpy()[:, list(heads)]
+    err = np.abs(got - ref[:, list(heads)])
+    return flops / dt / 1e12, dt, float(err.max()), float(err.mean())
+
+
+def decode_parity(bd):
+    import oracle
+
+    b = bd["cpu"]
+    ref, _ = oracle.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+                                 b["seq_lens"], 1.0 / math.sqrt(b["q"].shape[-1]))
+    err = np.abs(bd["o"].cpu().double().numpy() - ref)
+    return float(err.max()), float(err.mean())
+
+
+def headline(args, dev):
+    P_CFG = (1, 32, 8, 16384, 128, torch.bfloat16, 3)
+    D_CFG = dict(num_seqs=64, Hq=12, Hkv=2, d=128, lo=256, hi=4096, seed=4)
+    p = make_prefill(P_CFG, dev)
+    dsets = make_decode_sets(ROTATE, D_CFG["num_seqs"], D_CFG["Hq"], D_CFG["Hkv"], D_CFG["d"],
+                             D_CFG["lo"], D_CFG["hi"], D_CFG["seed"], dev)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_prefill(p)
+        run_decode(dsets[i % ROTATE])
+    torch.cuda.synchronize()
+
+    tp, td = Timer(), Timer()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        e = tp.start()
+        run_prefill(p)
+        tp.stop(e)
+        e = td.start()
+        run_decode(dsets[i % ROTATE])
+        td.stop(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    ms_p, ms_d = tp.mean_ms(), td.mean_ms()
+    fl = causal_flops(1, 32, 16384, 128)
+    tflops = fl / (ms_p * 1e-3) / 1e12
+    # decode: algorithmic bytes averaged over the rotated sets actually timed
+    used = [dsets[i % ROTATE] for i in range(args.steps)]
+    by = sum(decode_bytes(bd, 12, 2, 128) for bd in used) / len(used)
+    gbs = by / (ms_d * 1e-3) / 1e9
+
+    # parity on the timed outputs, and the oracle baseline (rank 0, N=1)
+    run_decode(dsets[0])
+    torch.cuda.synchronize()
+    dmax, dmean = decode_parity(dsets[0])
+    heads = tuple(range(0, 32, 2))  # 16 of the 32 query heads, every KV group
+    cpu_tflops, cpu_s, pmax, pmean = cpu_baseline_prefill(p, heads=heads)
+
+    return {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill bf16 B=1 Hq=32 Hkv=8 T=16384 d=128 + paged decode bf16 "
+                        "64 seqs x 1 query Hq=12 Hkv=2 d=128 block 16 L~U[256,4096] "
+                        f"({ROTATE} rotated KV pools)",
+            "prefill": {"B": 1, "Hq": 32, "Hkv": 8, "T": 16384, "d": 128, "causal": True},
+            "decode": {"num_seqs": 64, "Hq": 12, "Hkv": 2, "d": 128, "block_size": 16,
+                       "seq_len_range": [256, 4096],
+                       "partition_size": attn.decode_paged_partition_size(64, 2, max(
+                           bd["max_seq_len"] for bd in dsets))},
+        },
+        "prefill": {"ms": round(ms_p, 4), "tflops": round(tflops, 2),
+                    "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                    "max_abs_err_sampled_heads": pmax, "mean_abs_err_sampled_heads": pmean},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms_d, 5),
+                   "bytes": int(by), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                   "max_abs_err": dmax, "mean_abs_err": dmean},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": None},
+        "cpu_baseline": {"value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads(),
+                         "kind": "oracle",
+                         "sample": f"fp64 numpy oracle on the even query heads of the prefill "
+                                   f"({len(heads)} of 32 heads, all 16384 rows each), "
+                                   f"{cpu_s:.1f} s; credited causal FLOPs only"},
+    }
+
+
+def single(args, dev):
+    """Time one configuration alone (prefill configs 1-3, decode 4, mixed 5)."""
+    w = args.workload
+    if w in ("c1", "c2", "c3"):
+        cfg = {"c1": (1, 2, 2, 128, 64, torch.float32, 1),
+               "c2": (4, 16, 16, 2048, 128, torch.bfloat16, 2),
+               "c3": (1, 32, 8, 16384, 128, torch.bfloat16, 3)}[w]
+        p = make_prefill(cfg, dev)
+        for _ in range(args.warmup):
+            run_prefill(p)
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(args.steps):
+            e = t.start()
+            run_prefill(p)
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms()
+        fl = causal_flops(cfg[0], cfg[1], cfg[3], cfg[4])
+        peak = PEAK_F32_TFLOPS if cfg[5] == torch.float32 else PEAK_BF16_TFLOPS
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"workload": w, "ms": round(ms, 5), "tflops": round(tf, 3),
+                "frac_peak": round(tf / peak, 4), "dtype": str(cfg[5]).replace("torch.", "")}
+    if w == "c4":
+        dsets = make_decode_sets(ROTATE, 64, 12, 2, 128, 256, 4096, 4, dev)
+        for i in range(args.warmup):
+            run_decode(dsets[i % ROTATE])
+        torch.cuda.synchronize()
+        t = Timer()
+        for i in range(args.steps):
+            e = t.start()
+            run_decode(dsets[i % ROTATE])
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms()
+        used = [dsets[i % ROTATE] for i in range(args.steps)]
+        by = sum(decode_bytes(bd, 12, 2, 128) for bd in used) / len(used)
+        gbs = by / (ms * 1e-3) / 1e9
+        return {"workload": w, "ms": round(ms, 5), "gbs": round(gbs, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    if w == "c5":
+        # 8 chunks of 512 new tokens (no prior context) + 256 decodes,
+        # lengths uniform in [1024, 32768]; one shuffled pool on the GPU.
+        n_chunks, n_dec = 8, 256
+        g = torch.Generator().manual_seed(5)
+        dec_lens = torch.randint(1024, 32769, (n_dec,), generator=g).tolist()
+        seq_lens = [512] * n_chunks + dec_lens
+        q_lens = [512] * n_chunks + [1] * n_dec
+        b = inputs.paged_inputs(n_chunks + n_dec, 32, 8, 128, seq_lens=seq_lens, q_lens=q_lens,
+                                seed=5, device=dev, poison=False)
+        b["o"] = torch.empty_like(b["q"])
+        b["ws"] = torch.empty(attn.decode_paged_workspace_size(
+            n_chunks + n_dec, 32, 8, 128, b["max_seq_len"]), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            run_decode(b, with_qsl=True)
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(args.steps):
+            e = t.start()
+            run_decode(b, with_qsl=True)
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms()
+        fl = n_chunks * causal_flops(1, 32, 512, 128)
+        kv = sum(dec_lens) * 8 * 128 * 2 * 2 + n_chunks * 512 * 8 * 128 * 2 * 2
+        return {"workload": w, "ms": round(ms, 4), "chunk_gflop": round(fl / 1e9, 2),
+                "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
+    raise SystemExit(f"unknown workload {w}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "c1", "c2", "c3", "c4", "c5"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the path is not sharded "
+              "(see the multi-GPU design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    attn.load_library()
+    dev = torch.device("cuda:0")
+    if args.workload == "headline":
+        out = headline(args, dev)
+    else:
+        out = single(args, dev)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
