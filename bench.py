@@ -98,17 +98,20 @@ def make_decode_sets(n_sets, num_seqs, Hq, Hkv, d, lo, hi, seed, dev, q_lens=Non
         bd = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in b.items()}
         bd["o"] = torch.empty_like(bd["q"])
         bd["ws"] = torch.empty(max(1, attn.decode_paged_workspace_size(
-            num_seqs, Hq, Hkv, d, b["max_seq_len"])), dtype=torch.uint8, device=dev)
+            num_seqs, Hq, Hkv, d, b["max_seq_len"], PARTITION)), dtype=torch.uint8, device=dev)
         bd["cpu"] = b if r == 0 else None
         sets.append(bd)
     return sets
+
+
+PARTITION = 0  # split-KV partition length for the decode calls (0 = the library's choice)
 
 
 def run_decode(bd, with_qsl=False):
     attn.decode_paged(bd["q"], bd["k_cache"], bd["v_cache"], bd["block_table"], bd["seq_lens"],
                       max_seq_len=bd["max_seq_len"], max_query_len=bd["max_query_len"],
                       query_start_loc=bd["query_start_loc"] if with_qsl else None,
-                      o=bd["o"], workspace=bd["ws"])
+                      o=bd["o"], workspace=bd["ws"], partition_size=PARTITION)
 
 
 def blas_threads():
@@ -269,7 +272,8 @@ def single(args, dev):
         by = sum(decode_bytes(bd, 12, 2, 128) for bd in used) / len(used)
         gbs = by / (ms * 1e-3) / 1e9
         return {"workload": w, "ms": round(ms, 5), "gbs": round(gbs, 1),
-                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "partition_size": PARTITION or
+                attn.decode_paged_partition_size(64, 2, max(bd["max_seq_len"] for bd in dsets))}
     if w == "c5":
         # 8 chunks of 512 new tokens (no prior context) + 256 decodes,
         # lengths uniform in [1024, 32768]; one shuffled pool on the GPU.
@@ -282,7 +286,8 @@ def single(args, dev):
                                 seed=5, device=dev, poison=False)
         b["o"] = torch.empty_like(b["q"])
         b["ws"] = torch.empty(attn.decode_paged_workspace_size(
-            n_chunks + n_dec, 32, 8, 128, b["max_seq_len"]), dtype=torch.uint8, device=dev)
+            n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8,
+            device=dev)
         for _ in range(args.warmup):
             run_decode(b, with_qsl=True)
         torch.cuda.synchronize()
@@ -295,7 +300,8 @@ def single(args, dev):
         ms = t.mean_ms()
         fl = n_chunks * causal_flops(1, 32, 512, 128)
         kv = sum(dec_lens) * 8 * 128 * 2 * 2 + n_chunks * 512 * 8 * 128 * 2 * 2
-        return {"workload": w, "ms": round(ms, 4), "chunk_gflop": round(fl / 1e9, 2),
+        return {"workload": w, "ms": round(ms, 4), "partition_size": PARTITION,
+                "chunk_gflop": round(fl / 1e9, 2),
                 "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
     raise SystemExit(f"unknown workload {w}")
 
@@ -307,7 +313,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="split-KV partition length for decode (0: the library's choice)")
     args = ap.parse_args()
+    global PARTITION
+    PARTITION = args.partition_size
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the path is not sharded "
               "(see the multi-GPU design notes). Use --gpus 1.", file=sys.stderr)

@@ -98,7 +98,8 @@ int attn_decode_paged_partition_size(int num_seqs, int Hkv, int max_seq_len);
  * attn_decode_paged needs for the same arguments (partition_size as passed
  * to attn_decode_paged, 0 = automatic). Returns 0 if the arguments are out
  * of range. The workspace holds the fp32 split-KV partial results; its
- * contents need no initialisation and are garbage after the call.
+ * contents need no initialisation and are garbage after the call. Calls that
+ * run at the same time must not share a workspace.
  */
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
                                         int max_seq_len, int partition_size);
@@ -124,15 +125,16 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
  *                  query per sequence (row n) that sees all L_n keys.
  *   lse          : [num_tokens][Hq] fp32, optional (NULL = not written).
  *   workspace    : device memory of at least
- *                  attn_decode_paged_workspace_size(...) bytes (may be NULL
- *                  if that size is 0), 256-byte aligned.
+ *                  attn_decode_paged_workspace_size(...) bytes, 256-byte
+ *                  aligned.
  * Host-side bounds (the caller knows them; nothing is read back):
  *   max_seq_len   >= every L_n;  max_query_len >= every q_len_n (1 when
  *   query_start_loc is NULL);  max_blocks_per_seq >= ceil(max_seq_len/16).
  * Sequences with q_len_n == 1 take the split-KV decode path (partitions of
  * partition_size tokens, 0 = automatic, else a positive multiple of 16, then
  * a log-sum-exp merge); sequences with q_len_n >= 2 take the tiled prefill
- * path reading K/V tiles through the block table.
+ * path reading K/V tiles through the block table. partition_size is at most
+ * 4096 (larger: ATTN_ERR_UNSUPPORTED).
  * Preconditions not checked on the device: table entries for logical blocks
  * < ceil(L_n/16) lie in [0, num_blocks); 0 <= L_n <= max_seq_len;
  * q_len_n <= L_n; query_start_loc is non-decreasing with qsl[num_seqs] <=

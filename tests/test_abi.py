@@ -85,6 +85,7 @@ def decode(lib, q=P, kc=P2, vc=P3, table=P4, seq_lens=P4 + 0x10000, qsl=None, o=
     (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(table=None), NULL),
     (dict(seq_lens=None), NULL), (dict(o=None), NULL),
     (dict(dtype=F32), UNSUP), (dict(d=80), UNSUP), (dict(block_size=32), UNSUP),
+    (dict(partition_size=4096 + 16), UNSUP),
     (dict(Hq=34, Hkv=2), UNSUP), (dict(scale=0.0), UNSUP),
     (dict(num_seqs=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(max_seq_len=0), SHAPE),
     (dict(mbps=7), SHAPE), (dict(num_blocks=0), SHAPE), (dict(max_query_len=2), SHAPE),
@@ -106,8 +107,13 @@ def test_workspace_size_and_partition_policy():
     ws = attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 256)
     parts = 4096 // 256
     rows = 64 * 12 * parts
+    # partial outputs, then partial lse
     expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert ws == expect
+    assert attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 4096 + 16) == 0  # too long
+    for args in ((64, 2, 4096), (1, 1, 1), (256, 8, 32768), (3, 2, 100000)):
+        P = attn.decode_paged_partition_size(*args)
+        assert 16 <= P <= 4096 and P % 16 == 0
     assert attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 8) == 0    # not a multiple of 16
     assert attn.decode_paged_workspace_size(64, 12, 2, 96, 4096, 0) == 0     # d unsupported
     # automatic partition length: the workspace query and the launch agree

@@ -74,10 +74,13 @@ def test_partition_size_invariance():
     base_o, base_l = outs[-1]  # one partition per sequence: the unsplit case
     for o, l in outs[:-1]:
         # The merge identity is exact, but each partition rounds its weights
-        # P to bf16 against its own running max, so splits differ by that
-        # rounding (relative 2^-9 per weight), far below the oracle bound.
+        # P to bf16 against its own running max (relative 2^-9 per weight, so
+        # at most 2^-9 max|v| ~ 4e-3 on the output for N(0,1) values), and the
+        # two results are each rounded to bf16 (one ulp, 2^-8 |o|, apart at
+        # most). Both are far below the oracle bound.
         diff = (o.float() - base_o.float()).abs()
-        assert diff.max().item() <= 2e-3 and diff.mean().item() <= 2e-4
+        bound = base_o.float().abs() * 2.0 ** -8 + 4e-3
+        assert (diff <= bound).all() and diff.mean().item() <= 2e-4
         # lse sums unrounded fp32 weights: agreement to fp32 rounding
         assert torch.allclose(l, base_l, atol=1e-5, rtol=0)
 
@@ -129,3 +132,35 @@ def test_workspace_too_small_is_an_error():
         attn.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
                           max_seq_len=b["max_seq_len"], workspace=ws)
     assert e.value.status == -5
+
+
+
+def test_workspace_reuse_across_calls():
+    # One workspace serves several calls with different batches, filled with
+    # garbage first: its contents need no initialisation.
+    nseq, Hq, Hkv, d, max_len = 12, 8, 2, 128, 2000
+    ws = torch.full((attn.decode_paged_workspace_size(nseq, Hq, Hkv, d, max_len, 128),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+    for seed in (80, 81, 82):
+        b = inputs.paged_inputs(nseq, Hq, Hkv, d, seq_len_range=(1, max_len), seed=seed,
+                                max_blocks_per_seq=-(-max_len // 16))
+        bd = to_dev(b)
+        o = attn.decode_paged(bd["q"], bd["k_cache"], bd["v_cache"], bd["block_table"],
+                              bd["seq_lens"], max_seq_len=max_len, partition_size=128,
+                              workspace=ws)
+        torch.cuda.synchronize()
+        ro, _ = reference(b)
+        assert_close(o, ro, torch.bfloat16, f"reuse seed={seed}")
+
+
+def test_large_batch_partition_major_path():
+    # More than 1024 sequences: workgroups use the partition-major order
+    # instead of the packed item list; mix of lengths including empty.
+    n = 1100
+    lens = [((i * 37) % 300) for i in range(n)]
+    b = inputs.paged_inputs(n, 4, 2, 64, seq_lens=lens, seed=90)
+    for P in (0, 64):
+        o, lse = run(b, partition_size=P)
+        ro, rl = reference(b)
+        assert_close(o, ro, torch.bfloat16, f"1100 seqs P={P}")
+        assert_lse_close(lse, rl, f"1100 seqs P={P}")

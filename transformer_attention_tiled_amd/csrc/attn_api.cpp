@@ -35,13 +35,16 @@ struct WsLayout {
   int partition_size = 0;
   int max_parts = 0;
   size_t o_bytes = 0;
+  size_t l_bytes = 0;
   size_t total = 0;
 };
 
 bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partition_size,
                WsLayout* w) {
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || !supported_d(d)) return false;
-  if (partition_size < 0 || partition_size % attn::kBlockSize != 0) return false;
+  if (partition_size < 0 || partition_size % attn::kBlockSize != 0 ||
+      partition_size > attn::kMaxPartition)
+    return false;
   const int P = partition_size > 0 ? partition_size
                                    : attn::decode_partition_size(num_seqs, Hkv, max_seq_len);
   if (P <= 0) return false;
@@ -52,6 +55,7 @@ bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partit
   w->partition_size = P;
   w->max_parts = (int)parts;
   w->o_bytes = (size_t)o_bytes;
+  w->l_bytes = (size_t)l_bytes;
   w->total = (size_t)(o_bytes + l_bytes);
   return true;
 }
@@ -139,6 +143,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (query_start_loc == nullptr && (max_query_len != 1 || num_tokens < num_seqs))
     return ATTN_ERR_SHAPE;
   if (partition_size < 0 || partition_size % attn::kBlockSize != 0) return ATTN_ERR_SHAPE;
+  if (partition_size > attn::kMaxPartition) return ATTN_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4) ||
       !aligned(lse, 4) || !aligned(workspace, 256))

@@ -41,6 +41,7 @@ struct PagedArgs {
 };
 
 constexpr int kBlockSize = 16;
+constexpr int kMaxPartition = 4096;  // tokens per split-KV partition, at most
 
 // Host-side policy shared by the workspace query and the launch.
 int decode_partition_size(int num_seqs, int Hkv, int max_seq_len);

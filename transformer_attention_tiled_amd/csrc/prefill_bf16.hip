@@ -55,6 +55,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native vector types rather than HIP's struct-based vectors: they stay in
+// registers through inlining, where the struct types can end up in scratch.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -107,8 +111,8 @@ struct KvSrc<true> {
 };
 
 struct Prefetch {
-  uint4 k[4];
-  uint4 v[4];
+  u32x4 k[4];
+  u32x4 v[4];
 };
 
 __device__ __forceinline__ int sigma32(int i) {
@@ -116,7 +120,12 @@ __device__ __forceinline__ int sigma32(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// Global -> registers for key tile starting at n0 (rows >= kv_len read as zero).
+// Global -> registers for the key tile starting at n0. Rows past the last
+// key re-read the last key's row (kv_len >= 1 whenever a tile exists): the
+// loads stay unconditional and in bounds, never touch storage past the
+// sequence, and the copies are harmless because those keys' scores are
+// masked to -inf, so their weights are exactly 0 and their (finite) values
+// contribute exactly 0.
 template <int D, int NW, bool PAGED>
 __device__ __forceinline__ void load_tile(Prefetch& pf, const KvSrc<PAGED>& src, int n0,
                                           int kv_len, int tid) {
@@ -125,19 +134,15 @@ __device__ __forceinline__ void load_tile(Prefetch& pf, const KvSrc<PAGED>& src,
 #pragma unroll
   for (int i = 0; i < C::K_PASSES; ++i) {
     const int row = tid / C::NDC + i * C::K_ROWS;
-    const int key = n0 + row;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < kv_len) val = *(const uint4*)(src.k + src.template row_off<D>(key) + chunk * 8);
-    pf.k[i] = val;
+    const int key = min(n0 + row, kv_len - 1);
+    pf.k[i] = *(const u32x4*)(src.k + src.template row_off<D>(key) + chunk * 8);
   }
   const int dc = tid / C::NKG;
   const int kg = tid % C::NKG;
 #pragma unroll
   for (int i = 0; i < C::KPG; ++i) {
-    const int key = n0 + kg * C::KPG + i;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < kv_len) val = *(const uint4*)(src.v + src.template row_off<D>(key) + dc * 8);
-    pf.v[i] = val;
+    const int key = min(n0 + kg * C::KPG + i, kv_len - 1);
+    pf.v[i] = *(const u32x4*)(src.v + src.template row_off<D>(key) + dc * 8);
   }
 }
 
@@ -151,17 +156,17 @@ __device__ __forceinline__ void store_tile(const Prefetch& pf, char* stage, int 
 #pragma unroll
   for (int i = 0; i < C::K_PASSES; ++i) {
     const int row = tid / C::NDC + i * C::K_ROWS;
-    *(uint4*)(sk + row * C::KP + chunk * 16) = pf.k[i];
+    *(u32x4*)(sk + row * C::KP + chunk * 16) = pf.k[i];
   }
   const int dc = tid / C::NKG;
   const int kg = tid % C::NKG;
-  uint32_t w[4][4];
+  uint32_t w[4][4] = {};
 #pragma unroll
   for (int i = 0; i < C::KPG; ++i) {
-    w[i][0] = pf.v[i].x;
-    w[i][1] = pf.v[i].y;
-    w[i][2] = pf.v[i].z;
-    w[i][3] = pf.v[i].w;
+    w[i][0] = pf.v[i][0];
+    w[i][1] = pf.v[i][1];
+    w[i][2] = pf.v[i][2];
+    w[i][3] = pf.v[i][3];
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -176,7 +181,7 @@ __device__ __forceinline__ void store_tile(const Prefetch& pf, char* stage, int 
         e0 = w[0][j >> 1] & 0xffffu; e1 = w[1][j >> 1] & 0xffffu;
         e2 = w[2][j >> 1] & 0xffffu; e3 = w[3][j >> 1] & 0xffffu;
       }
-      *(uint2*)dst = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+      *(u32x2*)dst = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
     } else {
       uint32_t e0, e1;
       if (j & 1) {
@@ -227,9 +232,9 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
     const int qrow = wq0 + lq;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      uint4 val = make_uint4(0, 0, 0, 0);
+      u32x4 val = u32x4{0, 0, 0, 0};
       if (qrow < pb.q_len)
-        val = *(const uint4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf);
+        val = *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf);
       qf[s] = __builtin_bit_cast(bf16x8, val);
     }
   }
@@ -246,6 +251,11 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
     load_tile<D, NW, PAGED>(pf, src, 0, pb.kv_len, tid);
     store_tile<D, NW>(pf, lds, tid);
   }
+  // Every load of the prologue (Q fragments, first tile) has landed: with no
+  // load outstanding at the loop entry, the waits inside the loop only cover
+  // the prefetch of the next tile, which then overlaps the current tile's
+  // compute.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
@@ -304,16 +314,21 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
       const float mu = (m_run == kNegInf) ? 0.f : m_run;
       // weights p = 2^(s*c - m), row sum, and bf16 P^T fragments
       bf16x8 pk[4];
+      float part[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          float pv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * h + e], c, -mu));
-            l_run += p;
-            pk[2 * kb + h][e] = (__bf16)p;
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * h + e], c, -mu));
+            pk[2 * kb + h][e] = (__bf16)pv[e];
           }
+          // pairwise partial sums: short dependency chains
+          part[2 * kb + h] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        }
+      l_run += (part[0] + part[1]) + (part[2] + part[3]);
       // O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -349,7 +364,7 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
                             ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(uint2*)(orow + d0) = make_uint2(lo, hi);
+        *(u32x2*)(orow + d0) = u32x2{lo, hi};
       }
     if (pb.lse != nullptr && hf == 0)
       pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
