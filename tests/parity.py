@@ -2,7 +2,12 @@
 
 Tolerances: bf16 inputs with fp32 accumulation: max abs error <= 2e-2 and
 mean abs error <= 2e-3; fp32 path: max abs error <= 1e-4 (the stated bounds
-of the build). lse (fp32 in both kernels) is compared at 1e-3 absolute.
+of the build).
+
+lse: the bf16 kernels accumulate the row sum l over the weights after their
+rounding to bf16 (the very weights that multiply V), each within a relative
+2^-9 of the exact weight, so ln(l) is within 2^-9 of the exact log-sum-exp;
+the bound adds 1e-4 for fp32 arithmetic.
 """
 
 import numpy as np
@@ -11,7 +16,7 @@ import torch
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
 F32_MAX_ABS = 1e-4
-LSE_ABS = 1e-3
+LSE_ABS = 2.0 ** -9 + 1e-4
 
 
 def to64(t):

@@ -13,25 +13,48 @@
 // Work decomposition
 //   workgroup  = NW waves = (batch b | sequence n, query head h, tile of
 //                BM = 32*NW query rows); K/V head = h / (Hq/Hkv).
-//   key tile   = BN = 64 keys, staged in LDS (double buffered: the next
-//                tile's global loads are in flight while the current tile is
-//                computed).
+//   key tile   = BN = 64 keys. K and V tiles are copied from HBM straight
+//                into LDS (global_load_lds_dwordx4: each instruction moves
+//                one contiguous KiB, lane L's 16 bytes to M0 + 16 L), double
+//                buffered: the copies of tile j+1 are in flight while tile j
+//                is computed. Each lane's source offsets are fixed for the
+//                whole loop and the tile base is a scalar, so the copies cost
+//                no vector ALU work; only the ragged last tile clamps its
+//                rows to the last key.
 //   wave       = 32 query rows. The wave computes the TRANSPOSED scores
 //                S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that each lane
 //                owns one query column: the row max and row sum of the
-//                softmax are then in-lane reductions plus one exchange with
-//                the lane 32 apart. O^T = V^T P^T is the second MFMA chain;
-//                P^T is fed straight from the S^T accumulators (rounded to
-//                bf16), with no LDS round trip.
+//                softmax are in-lane reductions plus one exchange with the
+//                lane 32 apart. O^T = V^T P^T is the second MFMA chain; P^T
+//                is fed straight from the S^T accumulators (rounded to bf16).
+//
+// Why vector ALU work is the budget: on this chip VALU instructions do not
+// hide behind MFMA (issue is shared), so every VALU instruction per tile
+// costs MFMA throughput. The tile loop therefore keeps only the softmax on
+// the VALU: copies are DMA, the V^T operand comes from the LDS transpose
+// read ds_read_b64_tr_b16, and row sums use v_dot2_f32_bf16 on the packed
+// bf16 weights (two per instruction; summing the rounded weights also makes
+// the weights that multiply V sum exactly to the normaliser).
 //
 // MFMA 32x32x16 bf16 operand layout (checked on gfx950): lane l holds
 //   A[i = l%32][k = 8*(l/32) + e], B[k = 8*(l/32) + e][j = l%32], e = 0..7,
 //   C[i = 8*(r/4) + 4*(l/32) + r%4][j = l%32], r = 0..15.
-// The A rows of S^T are loaded in the order sigma(i) (bits 2 and 3 of i
+// The A rows of S^T are read in the order sigma(i) (bits 2 and 3 of i
 // swapped); then accumulator register r of key block kb in lane l holds key
 //   32*kb + 16*(r/8) + 8*(l/32) + r%8,
 // so registers 8h..8h+7 are exactly the B operand (keys 16h + 8*(l/32) + e)
-// of the P^T V^T product, and V^T is read from LDS as one 16-byte row piece.
+// of the P^T V^T product.
+//
+// ds_read_b64_tr_b16 (checked on gfx950): in each group of 16 lanes, lane
+// j = 4a + b receives element b of the 8-byte chunks addressed by lanes
+// 4r + a, r = 0..3. With lane i of a group addressing row K0 + i/4 at column
+// d0 + 4*(i%4), lane j receives V[K0..K0+3][d0 + j]: four consecutive keys
+// of one d column. Two such reads give the 8 keys of one V^T operand.
+//
+// LDS layout: K and V tiles row-major (one key per row), 16-byte chunks
+// XOR-swizzled per row with f(r) = 4*(r%4) + (r/4)%4, which spreads both the
+// K operand reads (16 rows, same chunk) and the transpose reads (4 rows, 4
+// adjacent chunks) over the banks.
 //
 // Online softmax (the pages say "updates the softmax statistics"; the
 // recurrence here is the standard running max / running sum): scores are
@@ -54,11 +77,12 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-// Native vector types rather than HIP's struct-based vectors: they stay in
-// registers through inlining, where the struct types can end up in scratch.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int BN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -70,20 +94,35 @@ template <int D, int NW>
 struct Cfg {
   static constexpr int NT = NW * 64;           // threads
   static constexpr int BM = NW * 32;           // query rows per workgroup
-  static constexpr int KP = D * 2 + 16;        // LDS pitch of a K row (bytes), padded
-  static constexpr int VP = BN * 2 + 16;       // LDS pitch of a V^T row (bytes), padded
-  static constexpr int K_BYTES = BN * KP;
-  static constexpr int V_BYTES = D * VP;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int NDC = D / 8;            // 16-byte chunks per row
-  static constexpr int K_ROWS = NT / NDC;      // K rows per load pass
-  static constexpr int K_PASSES = BN / K_ROWS;
-  static constexpr int NKG = NT / NDC;         // V key groups
-  static constexpr int KPG = BN / NKG;         // keys per V key group
-  static_assert(K_PASSES >= 1 && BN % K_ROWS == 0, "K tile mapping");
-  static_assert(KPG == 2 || KPG == 4, "V tile mapping");
+  static constexpr int ROW = D * 2;            // bytes per key row in LDS
+  static constexpr int NCH = D / 8;            // 16-byte chunks per row
+  static constexpr int TILE = BN * ROW;        // bytes of a K (or V) tile
+  static constexpr int STAGE = 2 * TILE;       // K tile then V tile
+  static constexpr int LDS = 2 * STAGE;        // double buffered
+  static constexpr int COPIES = TILE / 1024 / NW;  // KiB copies per wave per tile
+  static constexpr int RPC = 1024 / ROW;       // rows per KiB copy
+  static_assert(COPIES >= 1 && TILE % (1024 * NW) == 0, "tile copy split");
 };
+
+__device__ __forceinline__ int swz(int r, int nch) { return (4 * (r & 3) + ((r >> 2) & 3)) & (nch - 1); }
+
+__device__ __forceinline__ int sigma32(int i) {
+  // swap bits 2 and 3
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// HBM -> LDS copy, 16 bytes per lane to LDS address lds + 16 L.
+// Scalar 64-bit base + per-lane 32-bit byte offset.
+__device__ __forceinline__ void copy_saddr(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+// Per-lane 64-bit address.
+__device__ __forceinline__ void copy_vaddr(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_all_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Where a workgroup's K/V rows live.
 template <bool PAGED>
@@ -91,108 +130,17 @@ struct KvSrc;
 
 template <>
 struct KvSrc<false> {
-  const uint16_t* k;  // K[b][g] base, rows of D elements
-  const uint16_t* v;
-  template <int D>
-  __device__ __forceinline__ int64_t row_off(int key) const { return (int64_t)key * D; }
+  const char* k;  // K[b][g] row 0
+  const char* v;
 };
 
 template <>
 struct KvSrc<true> {
-  const uint16_t* k;  // cache base [num_blocks][Hkv][16][D], already offset by head g
-  const uint16_t* v;
+  const char* k;         // cache base [num_blocks][Hkv][16][D], offset by head g
+  const char* v;
   const int32_t* table;  // this sequence's block table row
-  int64_t block_stride;  // Hkv * 16 * D elements
-  template <int D>
-  __device__ __forceinline__ int64_t row_off(int key) const {
-    const int64_t phys = table[key >> 4];
-    return phys * block_stride + (int64_t)(key & 15) * D;
-  }
+  int64_t block_bytes;   // Hkv * 16 * D * 2
 };
-
-struct Prefetch {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-__device__ __forceinline__ int sigma32(int i) {
-  // swap bits 2 and 3
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-
-// Global -> registers for the key tile starting at n0. Rows past the last
-// key re-read the last key's row (kv_len >= 1 whenever a tile exists): the
-// loads stay unconditional and in bounds, never touch storage past the
-// sequence, and the copies are harmless because those keys' scores are
-// masked to -inf, so their weights are exactly 0 and their (finite) values
-// contribute exactly 0.
-template <int D, int NW, bool PAGED>
-__device__ __forceinline__ void load_tile(Prefetch& pf, const KvSrc<PAGED>& src, int n0,
-                                          int kv_len, int tid) {
-  using C = Cfg<D, NW>;
-  const int chunk = tid % C::NDC;
-#pragma unroll
-  for (int i = 0; i < C::K_PASSES; ++i) {
-    const int row = tid / C::NDC + i * C::K_ROWS;
-    const int key = min(n0 + row, kv_len - 1);
-    pf.k[i] = *(const u32x4*)(src.k + src.template row_off<D>(key) + chunk * 8);
-  }
-  const int dc = tid / C::NKG;
-  const int kg = tid % C::NKG;
-#pragma unroll
-  for (int i = 0; i < C::KPG; ++i) {
-    const int key = min(n0 + kg * C::KPG + i, kv_len - 1);
-    pf.v[i] = *(const u32x4*)(src.v + src.template row_off<D>(key) + dc * 8);
-  }
-}
-
-// Registers -> LDS: K row-major (padded), V transposed to V^T[d][key] (padded).
-template <int D, int NW>
-__device__ __forceinline__ void store_tile(const Prefetch& pf, char* stage, int tid) {
-  using C = Cfg<D, NW>;
-  char* sk = stage;
-  char* sv = stage + C::K_BYTES;
-  const int chunk = tid % C::NDC;
-#pragma unroll
-  for (int i = 0; i < C::K_PASSES; ++i) {
-    const int row = tid / C::NDC + i * C::K_ROWS;
-    *(u32x4*)(sk + row * C::KP + chunk * 16) = pf.k[i];
-  }
-  const int dc = tid / C::NKG;
-  const int kg = tid % C::NKG;
-  uint32_t w[4][4] = {};
-#pragma unroll
-  for (int i = 0; i < C::KPG; ++i) {
-    w[i][0] = pf.v[i][0];
-    w[i][1] = pf.v[i][1];
-    w[i][2] = pf.v[i][2];
-    w[i][3] = pf.v[i][3];
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // element j of each of the KPG rows, packed in key order
-    char* dst = sv + (dc * 8 + j) * C::VP + kg * C::KPG * 2;
-    if constexpr (C::KPG == 4) {
-      uint32_t e0, e1, e2, e3;
-      if (j & 1) {
-        e0 = w[0][j >> 1] >> 16; e1 = w[1][j >> 1] >> 16;
-        e2 = w[2][j >> 1] >> 16; e3 = w[3][j >> 1] >> 16;
-      } else {
-        e0 = w[0][j >> 1] & 0xffffu; e1 = w[1][j >> 1] & 0xffffu;
-        e2 = w[2][j >> 1] & 0xffffu; e3 = w[3][j >> 1] & 0xffffu;
-      }
-      *(u32x2*)dst = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-    } else {
-      uint32_t e0, e1;
-      if (j & 1) {
-        e0 = w[0][j >> 1] >> 16; e1 = w[1][j >> 1] >> 16;
-      } else {
-        e0 = w[0][j >> 1] & 0xffffu; e1 = w[1][j >> 1] & 0xffffu;
-      }
-      *(uint32_t*)dst = e0 | (e1 << 16);
-    }
-  }
-}
 
 // One workgroup's problem, resolved from the grid position.
 struct Problem {
@@ -207,12 +155,48 @@ struct Problem {
   int m0;             // first query row of this workgroup
 };
 
+// Copies of key tile n0 into LDS stage `stage` (LDS address). Every wave
+// copies COPIES KiB of K and of V. Rows past the last key re-read the last
+// key's row (never storage past the sequence); those keys are masked.
+template <int D, int NW, bool PAGED>
+__device__ __forceinline__ void copy_tile(const KvSrc<PAGED>& src, int n0, int kv_len,
+                                          uint32_t stage, int wave, int lane,
+                                          const uint32_t* off) {
+  using C = Cfg<D, NW>;
+  const bool full = n0 + BN <= kv_len;
+#pragma unroll
+  for (int s = 0; s < C::COPIES; ++s) {
+    const uint32_t lk = stage + (wave * C::COPIES + s) * 1024;
+    const uint32_t lv = lk + C::TILE;
+    const int t = (wave * C::COPIES + s) * C::RPC + lane / (C::ROW / 16);  // tile row
+    if constexpr (!PAGED) {
+      if (full) {
+        copy_saddr(src.k + (int64_t)n0 * C::ROW, off[s], lk);
+        copy_saddr(src.v + (int64_t)n0 * C::ROW, off[s], lv);
+      } else {
+        const int tc = min(t, kv_len - 1 - n0);
+        const uint32_t o = off[s] + (uint32_t)((tc - t) * C::ROW);
+        copy_saddr(src.k + (int64_t)n0 * C::ROW, o, lk);
+        copy_saddr(src.v + (int64_t)n0 * C::ROW, o, lv);
+      }
+    } else {
+      const int key = min(n0 + t, kv_len - 1);
+      const int64_t row = (int64_t)src.table[key >> 4] * src.block_bytes + (key & 15) * C::ROW;
+      const uint32_t inrow = off[s] - (uint32_t)(t * C::ROW);  // chunk byte offset
+      copy_vaddr(src.k + row + inrow, lk);
+      copy_vaddr(src.v + row + inrow, lv);
+    }
+  }
+}
+
 template <int D, int NW, bool PAGED, bool CAUSAL>
 __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& src, float c,
                                          char* lds) {
   using C = Cfg<D, NW>;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // the wave index is the same in every lane: say so, so that everything
+  // derived from it (copy destinations, tile bounds) stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;  // query column owned by this lane
   const int hf = lane >> 5;  // which half of the key rows
@@ -226,17 +210,27 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
   const int w_keys = wq0 >= pb.q_len ? 0 : (CAUSAL ? min(pb.kv_len, pb.ctx + w_last_q) : pb.kv_len);
   const int w_tiles = (w_keys + BN - 1) / BN;
 
+  // per-lane source byte offsets of the tile copies (tile-relative)
+  uint32_t off[C::COPIES];
+#pragma unroll
+  for (int s = 0; s < C::COPIES; ++s) {
+    const int lds_off = (wave * C::COPIES + s) * 1024 + 16 * lane;
+    const int t = lds_off / C::ROW;
+    const int pc = (lds_off % C::ROW) / 16;
+    off[s] = (uint32_t)(t * C::ROW + ((pc ^ swz(t, C::NCH)) * 16));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  if (n_tiles > 0) copy_tile<D, NW, PAGED>(src, 0, pb.kv_len, lds0, wave, lane, off);
+
   // Q^T fragments: B operand, lane holds Q[wq0 + lq][16*s + 8*hf + e]
   bf16x8 qf[D / 16];
   {
-    const int qrow = wq0 + lq;
+    const int qrow = min(wq0 + lq, pb.q_len - 1);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (qrow < pb.q_len)
-        val = *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf);
-      qf[s] = __builtin_bit_cast(bf16x8, val);
-    }
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf));
   }
 
   f32x16 acc[D / 32];
@@ -245,35 +239,40 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
   float m_run = kNegInf;  // reference max, log2 units
   float l_run = 0.f;      // partial row sum over this lane's keys
   const int qpos = pb.ctx + wq0 + lq;  // absolute position of this lane's query
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  Prefetch pf;
-  if (n_tiles > 0) {
-    load_tile<D, NW, PAGED>(pf, src, 0, pb.kv_len, tid);
-    store_tile<D, NW>(pf, lds, tid);
-  }
-  // Every load of the prologue (Q fragments, first tile) has landed: with no
-  // load outstanding at the loop entry, the waits inside the loop only cover
-  // the prefetch of the next tile, which then overlaps the current tile's
-  // compute.
+  // K operand rows of the two 32-key blocks (sigma order) and the lane's
+  // position in its group of 16 for the transpose reads
+  const int krow0 = sigma32(lq);
+  const int g16 = lane >> 4, i16 = lane & 15;
+
+  // Q landed and the first tile's copies are done everywhere.
   __builtin_amdgcn_s_waitcnt(0);
+  wait_all_copies();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int n0 = j * BN;
-    if (j + 1 < n_tiles) load_tile<D, NW, PAGED>(pf, src, n0 + BN, pb.kv_len, tid);
+    const uint32_t cur = lds0 + (j & 1) * C::STAGE;
+    if (j + 1 < n_tiles)
+      copy_tile<D, NW, PAGED>(src, n0 + BN, pb.kv_len, lds0 + ((j + 1) & 1) * C::STAGE, wave,
+                              lane, off);
 
     if (j < w_tiles) {
-      const char* sk = lds + (j & 1) * C::STAGE;
-      const char* sv = sk + C::K_BYTES;
+      const lds_char* sk = (const lds_char*)(uintptr_t)cur;
+      const lds_char* sv = sk + C::TILE;
       // S^T = K Q^T for 2 blocks of 32 keys
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const char* kp = sk + (32 * kb + sigma32(lq)) * C::KP + hf * 16;
+        const int r = 32 * kb + krow0;
+        const lds_char* kp = sk + r * C::ROW;
+        const int sw = swz(r, C::NCH);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-          const bf16x8 a = *(const bf16x8*)(kp + st * 32);
+          const bf16x8 a = *(const bf16x8 __attribute__((address_space(3)))*)(
+              kp + (((2 * st + hf) ^ sw) * 16));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
         }
       }
@@ -312,36 +311,50 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
       const float mu = (m_run == kNegInf) ? 0.f : m_run;
-      // weights p = 2^(s*c - m), row sum, and bf16 P^T fragments
+      // weights p = 2^(s*c - m) rounded to bf16, and their sum
       bf16x8 pk[4];
-      float part[4];
+      float part[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float pv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * h + e], c, -mu));
-            pk[2 * kb + h][e] = (__bf16)pv[e];
+          for (int e = 0; e < 8; ++e)
+            pk[2 * kb + h][e] =
+                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * h + e], c, -mu));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pp = {pk[2 * kb + h][e], pk[2 * kb + h][e + 1]};
+            part[h] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, part[h], false);
           }
-          // pairwise partial sums: short dependency chains
-          part[2 * kb + h] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         }
-      l_run += (part[0] + part[1]) + (part[2] + part[3]);
-      // O^T += V^T P^T
+      l_run += part[0] + part[1];
+      // O^T += V^T P^T; V^T operand: two transpose reads of 4 keys each
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const char* vp = sv + (32 * db + lq) * C::VP + hf * 16;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(vp + kk * 32);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], acc[db], 0, 0, 0);
+          u32x2 half[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 16 * kk + 8 * (g16 >> 1) + 4 * hh + (i16 >> 2);
+            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);  // element
+            const lds_char* p =
+                sv + row * C::ROW + ((((col >> 3) ^ swz(row, C::NCH)) * 16) + (col & 7) * 2);
+            half[hh] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (s16x4 __attribute__((address_space(3)))*)p));
+          }
+          const u32x4 both = {half[0][0], half[0][1], half[1][0], half[1][1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                            pk[kk], acc[db], 0, 0, 0);
         }
       }
     }
 
-    if (j + 1 < n_tiles) store_tile<D, NW>(pf, lds + ((j + 1) & 1) * C::STAGE, tid);
+    // this wave's copies of tile j+1 have landed; after the barrier every
+    // wave's have, and nobody reads tile j any more
+    wait_all_copies();
     __syncthreads();
   }
 
@@ -356,15 +369,11 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        __bf16 b0 = (__bf16)(acc[db][4 * g4 + 0] * inv);
-        __bf16 b1 = (__bf16)(acc[db][4 * g4 + 1] * inv);
-        __bf16 b2 = (__bf16)(acc[db][4 * g4 + 2] * inv);
-        __bf16 b3 = (__bf16)(acc[db][4 * g4 + 3] * inv);
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(u32x2*)(orow + d0) = u32x2{lo, hi};
+        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 0] * inv));
+        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 1] * inv));
+        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 2] * inv));
+        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 3] * inv));
+        *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
       }
     if (pb.lse != nullptr && hf == 0)
       pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
@@ -399,7 +408,7 @@ __device__ __forceinline__ void logical_to_work(int logical, int units, int n_qt
 
 template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a, float c, int n_qt) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg<D, NW>::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg<D, NW>::LDS];
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   int unit, qt;
   logical_to_work(logical, a.B * a.Hq, n_qt, unit, qt);
@@ -418,8 +427,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
   pb.ctx = 0;
   pb.m0 = qt * Cfg<D, NW>::BM;
   KvSrc<false> src;
-  src.k = (const uint16_t*)a.k + kvoff;
-  src.v = (const uint16_t*)a.v + kvoff;
+  src.k = (const char*)((const uint16_t*)a.k + kvoff);
+  src.v = (const char*)((const uint16_t*)a.v + kvoff);
   run_tile<D, NW, false, CAUSAL>(pb, src, c, lds);
 }
 
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void paged_prefill_bf16_kernel(PagedArgs a, float c,
                                                                           int n_qt) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg<D, NW>::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg<D, NW>::LDS];
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   int unit, qt;
   logical_to_work(logical, a.num_seqs * a.Hq, n_qt, unit, qt);
@@ -449,10 +458,10 @@ __global__ __launch_bounds__(NW * 64, 2) void paged_prefill_bf16_kernel(PagedArg
   pb.ctx = L - q_len;
   pb.m0 = qt * Cfg<D, NW>::BM;
   KvSrc<true> src;
-  src.k = (const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D;
-  src.v = (const uint16_t*)a.v_cache + (int64_t)g * kBlockSize * D;
+  src.k = (const char*)((const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D);
+  src.v = (const char*)((const uint16_t*)a.v_cache + (int64_t)g * kBlockSize * D);
   src.table = a.block_table + (int64_t)n * a.max_blocks_per_seq;
-  src.block_stride = (int64_t)a.Hkv * kBlockSize * D;
+  src.block_bytes = (int64_t)a.Hkv * kBlockSize * D * 2;
   run_tile<D, NW, true, true>(pb, src, c, lds);
 }
 
