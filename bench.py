@@ -278,12 +278,9 @@ def single(args, dev):
         # 8 chunks of 512 new tokens (no prior context) + 256 decodes,
         # lengths uniform in [1024, 32768]; one shuffled pool on the GPU.
         n_chunks, n_dec = 8, 256
-        g = torch.Generator().manual_seed(5)
-        dec_lens = torch.randint(1024, 32769, (n_dec,), generator=g).tolist()
-        seq_lens = [512] * n_chunks + dec_lens
-        q_lens = [512] * n_chunks + [1] * n_dec
-        b = inputs.paged_inputs(n_chunks + n_dec, 32, 8, 128, seq_lens=seq_lens, q_lens=q_lens,
-                                seed=5, device=dev, poison=False)
+        b = inputs.mixed_batch_inputs(n_chunks, 512, n_dec, (1024, 32768), 32, 8, 128, seed=5,
+                                      device=dev)
+        dec_lens = b["seq_lens_host"][n_chunks:]
         b["o"] = torch.empty_like(b["q"])
         b["ws"] = torch.empty(attn.decode_paged_workspace_size(
             n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8,

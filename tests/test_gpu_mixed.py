@@ -73,3 +73,32 @@ def test_chunk_rows_match_contiguous_prefill():
     a = o.float().cpu().permute(1, 0, 2)
     c = op[0, :, L - q_len:].float().cpu()
     assert (a - c).abs().max().item() <= 2e-2
+
+
+def test_config_mixed_batch_full_size_sampled():
+    # 8 chunks of 512 new tokens + 256 decodes with lengths uniform in
+    # [1024, 32768], Hq=32, Hkv=8, d=128, one shuffled pool (~17.9 GB) drawn
+    # on the GPU; the call is the one the benchmark times. The oracle checks
+    # every chunk and 16 decode sequences including the shortest and longest.
+    print("[mixed] full-size batch", flush=True)
+    b = inputs.mixed_batch_inputs(8, 512, 256, (1024, 32768), 32, 8, 128, seed=5, device=DEV)
+    o = torch.empty_like(b["q"])
+    lse = torch.full(tuple(b["q"].shape[:2]), float("nan"), device=DEV)
+    attn.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                      max_seq_len=b["max_seq_len"], max_query_len=b["max_query_len"],
+                      query_start_loc=b["query_start_loc"], o=o, lse=lse)
+    torch.cuda.synchronize()
+    lens = b["seq_lens_host"]
+    dec = list(range(8, 264))
+    rng = np.random.default_rng(5)
+    pick = {min(dec, key=lambda n: lens[n]), max(dec, key=lambda n: lens[n])}
+    pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
+    seqs = list(range(8)) + sorted(pick)
+    kc, vc, table, sl, q, qsl = inputs.compact_sequences(b, seqs)
+    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl)
+    qsl_full = b["query_start_loc"].cpu()
+    rows = torch.cat([torch.arange(int(qsl_full[n]), int(qsl_full[n + 1])) for n in seqs])
+    assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "full-size mixed")
+    assert_lse_close(lse[rows.to(DEV)], rl, "full-size mixed")
+    del b
+    torch.cuda.empty_cache()

@@ -144,3 +144,52 @@ def permute_blocks(batch, seed):
     t = batch["block_table"].cpu().to(torch.int64)
     t_new = torch.where(t >= 0, pi[t.clamp(min=0)], t).to(torch.int32)
     return k_new, v_new, t_new.to(batch["block_table"].device)
+
+
+def mixed_batch_inputs(n_chunks=8, chunk_len=512, n_decode=256, decode_len_range=(1024, 32768),
+                       Hq=32, Hkv=8, d=128, seed=5, device="cpu", poison=False):
+    """Mixed paged batch: ``n_chunks`` prefill chunks of ``chunk_len`` new
+    tokens (no prior context, their K/V already in the pool) followed by
+    ``n_decode`` single-token decodes whose lengths are uniform integers in
+    ``decode_len_range`` (drawn on the CPU from ``seed``). One shuffled pool
+    holds every sequence; on ``device="cuda"`` the values are drawn there.
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    lo, hi = decode_len_range
+    dec_lens = torch.randint(lo, hi + 1, (n_decode,), generator=g).tolist()
+    seq_lens = [chunk_len] * n_chunks + dec_lens
+    q_lens = [chunk_len] * n_chunks + [1] * n_decode
+    return paged_inputs(n_chunks + n_decode, Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens,
+                        seed=seed, device=device, poison=poison)
+
+
+def compact_sequences(batch, seqs):
+    """CPU copy of just the physical blocks that the given sequences use.
+
+    Returns (k_cache, v_cache, block_table, seq_lens, q, query_start_loc) on
+    the CPU for the sub-batch ``seqs`` (in that order), with the table
+    rewritten onto the compact pool. Only data movement: nothing is computed.
+    """
+    table = batch["block_table"].cpu()
+    lens = batch["seq_lens"].cpu()
+    qsl = batch["query_start_loc"].cpu()
+    used, rows = [], []
+    for n in seqs:
+        nb = math.ceil(int(lens[n]) / BLOCK_SIZE)
+        rows.append((len(used), nb))
+        used.extend(int(x) for x in table[n, :nb])
+    idx = torch.tensor(used, dtype=torch.int64)
+    dev = batch["k_cache"].device
+    k = batch["k_cache"][idx.to(dev)].cpu()
+    v = batch["v_cache"][idx.to(dev)].cpu()
+    width = max(nb for _, nb in rows)
+    new_table = torch.full((len(seqs), max(1, width)), -1, dtype=torch.int32)
+    for i, (start, nb) in enumerate(rows):
+        new_table[i, :nb] = torch.arange(start, start + nb, dtype=torch.int32)
+    q_parts, new_qsl = [], [0]
+    for n in seqs:
+        t0, t1 = int(qsl[n]), int(qsl[n + 1])
+        q_parts.append(batch["q"][t0:t1].cpu())
+        new_qsl.append(new_qsl[-1] + (t1 - t0))
+    return (k, v, new_table, lens[list(seqs)].to(torch.int32), torch.cat(q_parts),
+            torch.tensor(new_qsl, dtype=torch.int32))
