@@ -114,6 +114,21 @@ def run_decode(bd, with_qsl=False):
                       o=bd["o"], workspace=bd["ws"], partition_size=PARTITION)
 
 
+def measured_traffic(kernel_key):
+    """Calibrated HBM bytes per launch recorded under profiles/ for a kernel,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[kernel_key]
+        src = os.path.join(ROOT, "transformer_attention_tiled_amd", "csrc", rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return int(rec["fetch_bytes"] + rec["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -221,10 +236,12 @@ def headline(args, dev):
                    "max_abs_err": dmax, "mean_abs_err": dmean},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(
+                         "prefill_bf16_kernel<128,4,true> B=1 Hq=32 Hkv=8 T=16384")},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": None},
+                            "traffic": measured_traffic(
+                                "decode_kernel<128> 64 seqs Hq=12 Hkv=2 (mean of 4 rotated pools)")},
         "cpu_baseline": {"value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads(),
                          "kind": "oracle",
                          "sample": f"fp64 numpy oracle on the even query heads of the prefill "
@@ -300,6 +317,24 @@ def single(args, dev):
         return {"workload": w, "ms": round(ms, 4), "partition_size": PARTITION,
                 "chunk_gflop": round(fl / 1e9, 2),
                 "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
+    if w == "copy":
+        # plain 1 GiB device-to-device copy: the calibration for the HBM byte
+        # counters (what FETCH_SIZE / WRITE_SIZE read for a known size)
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(args.steps):
+            e = t.start()
+            dst.copy_(src)
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms()
+        return {"workload": w, "bytes_each_way": n, "ms": round(ms, 4),
+                "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
     raise SystemExit(f"unknown workload {w}")
 
 
@@ -309,7 +344,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "c1", "c2", "c3", "c4", "c5"])
+                    choices=["headline", "c1", "c2", "c3", "c4", "c5", "copy"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition length for decode (0: the library's choice)")
     args = ap.parse_args()
