@@ -71,6 +71,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -380,6 +382,412 @@ __device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-group schedule. On gfx950 the vector ALU work of one wave runs alongside
+// the MFMA work of another wave on the same SIMD, but hardly alongside the
+// MFMA work of its own instruction stream. So the workgroup has 8 waves in
+// two groups of 4 (waves w and w+4 share a SIMD) that run half a tile apart,
+// separated by workgroup barriers: while one group does the products of a
+// tile (M phase: O += P V for the previous tile, then S^T = K Q^T for this
+// one), the other does the softmax of its tile (S phase), then they swap.
+//
+//   phase t:     0      1      2      3      4     ...
+//   group 0:    M(0)   S(0)   M(1)   S(1)   M(2)
+//   group 1:     -     M(0)   S(0)   M(1)   S(1)
+//
+// K and V tiles live in four LDS buffers each. At the start of its S(j)
+// each wave issues its share of the copies of K tile j+3 and V tile j+2,
+// so the M phase holds nothing but LDS reads and MFMAs; at the end of M(j)
+// it waits for its own copies of K tile j+1 and V tile j (issued in
+// S(j-2)). The barrier that follows the later group's M(j) therefore
+// publishes both tiles to every wave before either group starts M(j+1). The
+// buffer a copy overwrites was last read in M(j-1) of both groups, which
+// ended before an earlier barrier.
+//
+// A workgroup covers 256 query rows; the two waves on SIMD s own rows
+// 64s .. 64s+31 (group 0) and 64s+32 .. 64s+63 (group 1), so both stop at the
+// same key tile.
+
+constexpr int kPPW = 8;       // waves per workgroup
+constexpr int kPPBM = 256;    // query rows per workgroup
+constexpr int kBufs = 4;      // LDS buffers for K tiles (and as many for V)
+
+template <int D>
+struct PP {
+  static constexpr int ROW = D * 2;
+  static constexpr int NCH = D / 8;
+  static constexpr int TILE = BN * ROW;          // bytes of one K or V tile
+  static constexpr int LDS = 2 * kBufs * TILE;   // 128 KiB at D = 128
+  static constexpr int CP = TILE / 1024 / kPPW;  // KiB copies per wave per tile
+  static constexpr int RPC = 1024 / ROW;         // rows per KiB copy
+  static_assert(CP >= 1 && TILE % (1024 * kPPW) == 0, "tile copy split");
+};
+
+// V tiles use their own swizzle: chunk c of row r sits at chunk c ^ vswz(r),
+// which moves each of 4 consecutive rows (D = 128; 2 pairs of rows at D = 64)
+// into its own quarter of the 64 banks. A transpose read touches 4 rows x
+// 64 bytes per 32 lanes, so it is conflict free, and its address is one
+// per-lane base per 32-column block plus immediates for the row offsets.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses and keeps the compiler from
+// moving any instruction across it (the two groups' phases must not blur).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// This wave's share of the copies of one K or V tile (rows n0 .. n0+63) into
+// the LDS buffer at `buf`. Rows past the last key re-read the last key's row.
+template <int D, bool PAGED>
+__device__ __forceinline__ void pp_copy(const char* base, const KvSrc<PAGED>& src, int n0,
+                                        int kv_len, uint32_t buf, int wave, int lane,
+                                        const uint32_t* off) {
+  using C = PP<D>;
+  const bool full = n0 + BN <= kv_len;
+#pragma unroll
+  for (int s = 0; s < C::CP; ++s) {
+    const uint32_t l = buf + (wave * C::CP + s) * 1024;
+    const int t = (wave * C::CP + s) * C::RPC + lane / (C::ROW / 16);  // tile row
+    if constexpr (!PAGED) {
+      if (full) {
+        copy_saddr(base + (int64_t)n0 * C::ROW, off[s], l);
+      } else {
+        const int tc = min(t, kv_len - 1 - n0);
+        copy_saddr(base + (int64_t)n0 * C::ROW, off[s] + (uint32_t)((tc - t) * C::ROW), l);
+      }
+    } else {
+      const int key = min(n0 + t, kv_len - 1);
+      const int64_t row = (int64_t)src.table[key >> 4] * src.block_bytes + (key & 15) * C::ROW;
+      copy_vaddr(base + row + (off[s] - (uint32_t)(t * C::ROW)), l);
+    }
+  }
+}
+
+// Steady-state copy of a full tile: `tile` is the tile's first row in HBM,
+// `dst` this wave's first KiB in the LDS buffer.
+template <int D>
+__device__ __forceinline__ void pp_copy_full(const char* tile, uint32_t dst, const uint32_t* off) {
+  using C = PP<D>;
+#pragma unroll
+  for (int s = 0; s < C::CP; ++s) copy_saddr(tile, off[s], dst + s * 1024);
+}
+
+// M phase: O^T += V^T P^T over the previous tile (16 MFMAs at D = 128), then
+// S^T = K Q^T for this tile (16 MFMAs). The instruction order is pinned so
+// that the LDS operand reads run LOOKAHEAD MFMAs ahead of their MFMA: the
+// other wave on the SIMD is in its softmax phase meanwhile, so any MFMA that
+// waits for LDS leaves the matrix core idle.
+// kabs / vabs: per-lane LDS addresses within K buffer 0 / V buffer 0; KOFF
+// and VOFF select the buffers and become instruction offsets, so the phase
+// needs no vector ALU work for addressing.
+template <int D, bool DO_PV, bool DO_S, int KOFF, int VOFF>
+__device__ __forceinline__ void m_phase(f32x16* acc, f32x16* sc, const bf16x8* pk,
+                                        const bf16x8* qf, const uint32_t* vabs,
+                                        const uint32_t* kabs) {
+  using C = PP<D>;
+  constexpr int LOOKAHEAD = 8;
+  constexpr int NPV = DO_PV ? 4 * (D / 32) : 0;  // MFMAs, 2 transpose reads each
+  constexpr int NS = DO_S ? 2 * (D / 16) : 0;    // MFMAs, 1 b128 read each
+  if constexpr (DO_PV) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        u32x2 half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const lds_char* p =
+              (const lds_char*)(uintptr_t)vabs[db] + (VOFF + (16 * kk + 4 * hh) * C::ROW);
+          half[hh] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (s16x4 __attribute__((address_space(3)))*)p));
+        }
+        const u32x4 both = {half[0][0], half[0][1], half[1][0], half[1][1]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                          pk[kk], acc[db], 0, 0, 0);
+      }
+    }
+  }
+  if constexpr (DO_S) {
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const bf16x8 __attribute__((address_space(3)))*)(
+            (const lds_char*)(uintptr_t)kabs[s] + (KOFF + 32 * kb * C::ROW));
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
+      }
+    }
+  }
+  // pinned order: reads of the first LOOKAHEAD MFMAs, then MFMA k followed by
+  // the reads of MFMA k + LOOKAHEAD
+  constexpr int N = NPV + NS;
+  constexpr int first = (LOOKAHEAD < NPV ? 2 * LOOKAHEAD : 2 * NPV) +
+                        (LOOKAHEAD > NPV ? (LOOKAHEAD - NPV < NS ? LOOKAHEAD - NPV : NS) : 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const int nx = k + LOOKAHEAD;
+    if (nx < NPV)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else if (nx < N)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <int D, bool PAGED, bool CAUSAL>
+__device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& src, float c,
+                                       char* lds) {
+  using C = PP<D>;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;  // query column owned by this lane
+  const int hf = lane >> 5;  // which half of the key rows
+  const int grp = wave >> 2;
+  const int wq0 = pb.m0 + 64 * (wave & 3) + 32 * grp;
+
+  const int wg_last_q = min(pb.m0 + kPPBM, pb.q_len);
+  const int wg_keys = CAUSAL ? min(pb.kv_len, pb.ctx + wg_last_q) : pb.kv_len;
+  const int n = (wg_keys + BN - 1) / BN;
+  const int w_last_q = min(wq0 + 32, pb.q_len);
+  const int w_keys =
+      wq0 >= pb.q_len ? 0 : (CAUSAL ? min(pb.kv_len, pb.ctx + w_last_q) : pb.kv_len);
+  const int wt = (w_keys + BN - 1) / BN;  // tiles this wave computes (<= n)
+
+  // per-lane source offsets of the copies (tile-relative): K and V tiles
+  // are swizzled differently
+  uint32_t koff[C::CP], voff[C::CP];
+#pragma unroll
+  for (int s = 0; s < C::CP; ++s) {
+    const int lds_off = (wave * C::CP + s) * 1024 + 16 * lane;
+    const int t = lds_off / C::ROW;
+    const int pc = (lds_off % C::ROW) / 16;
+    koff[s] = (uint32_t)(t * C::ROW + ((pc ^ swz(t, C::NCH)) * 16));
+    voff[s] = (uint32_t)(t * C::ROW + ((pc ^ vswz<D>(t)) * 16));
+  }
+  // LDS read offsets (buffer-relative). K operand of key block kb and
+  // k-step s: row 32 kb + sigma(lq), chunk (2 s + hf) ^ swz(row); the kb
+  // part is an immediate. V^T operand of column block db: rows
+  // 16 kk + 8 (g16 / 2) + 4 hh + i16 / 4 (kk, hh immediates).
+  const int krow0 = sigma32(lq);
+  const int g16 = lane >> 4, i16 = lane & 15;
+  uint32_t kaddr[D / 16], vaddr[D / 32];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    kaddr[s] = (uint32_t)(krow0 * C::ROW + (((2 * s + hf) ^ swz(krow0, C::NCH)) * 16));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int row = 8 * (g16 >> 1) + (i16 >> 2);
+    const int chunk = 4 * db + 2 * (g16 & 1) + ((i16 >> 1) & 1);
+    vaddr[db] = (uint32_t)(row * C::ROW + 16 * (chunk ^ vswz<D>(row)) + 8 * (i16 & 1));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto kbuf = [&](int j) { return lds0 + (uint32_t)((j % kBufs) * C::TILE); };
+  auto vbuf = [&](int j) { return lds0 + (uint32_t)((kBufs + j % kBufs) * C::TILE); };
+  // (the empty asm keeps the addresses in registers: recomputing them from
+  // the lane id in every tile would cost vector ALU time in the M phase)
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kaddr[s] += lds0;
+    asm volatile("" : "+v"(kaddr[s]));
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    vaddr[db] += lds0 + kBufs * C::TILE;
+    asm volatile("" : "+v"(vaddr[db]));
+  }
+
+  // K tile 0 and the Q^T fragments (B operand, lane holds
+  // Q[wq0 + lq][16*s + 8*hf + e]); both are waited for before the first
+  // phase, then K tiles 1, 2 and V tiles 0, 1 are put in flight (in the
+  // order the waits in the loop assume: K1, V0, then K2, V1).
+  pp_copy<D, PAGED>(src.k, src, 0, pb.kv_len, kbuf(0), wave, lane, koff);
+  bf16x8 qf[D / 16];
+  {
+    const int qrow = min(wq0 + lq, pb.q_len - 1);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (1 < n) pp_copy<D, PAGED>(src.k, src, BN, pb.kv_len, kbuf(1), wave, lane, koff);
+  pp_copy<D, PAGED>(src.v, src, 0, pb.kv_len, vbuf(0), wave, lane, voff);
+  if (2 < n) pp_copy<D, PAGED>(src.k, src, 2 * BN, pb.kv_len, kbuf(2), wave, lane, koff);
+  if (1 < n) pp_copy<D, PAGED>(src.v, src, BN, pb.kv_len, vbuf(1), wave, lane, voff);
+  {
+    // M(0) multiplies P = 0 with the V buffer of "tile -1": make it zeros
+    // (V tile 3, the first copy into that buffer, is issued in S(1), after
+    // two more barriers)
+    constexpr int PER = C::TILE / (kPPW * 64);  // bytes per thread
+    lds_char* z = (lds_char*)(uintptr_t)(vbuf(kBufs - 1) + tid * PER);
+#pragma unroll
+    for (int i = 0; i < PER / 16; ++i)
+      *(u32x4 __attribute__((address_space(3)))*)(z + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  }
+  phase_barrier();
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
+  bf16x8 pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
+  float m_run = kNegInf;  // reference max, log2 units
+  float l_run = 0.f;      // partial row sum over this lane's keys
+  const int qpos = pb.ctx + wq0 + lq;
+
+  // Both groups run the same sequence M(j), barrier, S(j), barrier; group 1
+  // starts one barrier later (and group 0 ends with one), which puts the two
+  // groups half a tile apart.
+  const int n_full = pb.kv_len / BN;                          // tiles without a ragged end
+  const uint32_t wdst = (uint32_t)(wave * C::CP * 1024);       // this wave's part of a tile
+  if (grp == 1) phase_barrier();
+  // one step per key tile; the buffer index B = j % 4 is a template constant
+  // in each of the four unrolled copies, so LDS offsets are immediates
+  auto step = [&](const int j, auto bconst) {
+    constexpr int B = decltype(bconst)::value;
+    // ---- M(j): O^T += V^T P^T (tile j-1), then S^T = K Q^T (tile j).
+    // Always both products, so the phase is one block: before the first
+    // tile P is 0 and the V buffer read is zero-filled; after the wave's
+    // last tile P is 0; a product of K with a buffer that holds no tile of
+    // this workgroup yet is computed and ignored.
+    m_phase<D, true, true, B * C::TILE, ((B + kBufs - 1) % kBufs) * C::TILE>(acc, sc, pk, qf,
+                                                                             vaddr, kaddr);
+    // this wave's copies of K tile j+1 and V tile j (issued at the start of
+    // S(j-2)) have landed; the barrier after the later group's M(j) makes
+    // every wave's copies visible before either group's M(j+1). Only the
+    // copies issued in S(j-1) may still be in flight.
+    if (j + 2 < n)
+      wait_copies<2 * C::CP>();
+    else if (j + 1 < n)
+      wait_copies<C::CP>();
+    else
+      wait_copies<0>();
+    phase_barrier();
+
+    // ---- S(j): copies of K tile j+3 and V tile j+2 first (their buffers
+    // held K tile j-1 and V tile j-2, last read in M(j-1) of both groups,
+    // before the previous barrier), then mask, running max, weights, sums.
+    if (j + 3 < n) {
+      const uint32_t buf = lds0 + (uint32_t)(((B + 3) % kBufs) * C::TILE);
+      if (!PAGED && j + 3 < n_full)
+        pp_copy_full<D>(src.k + (int64_t)(j + 3) * C::TILE, buf + wdst, koff);
+      else
+        pp_copy<D, PAGED>(src.k, src, (j + 3) * BN, pb.kv_len, buf, wave, lane, koff);
+    }
+    if (j + 2 < n) {
+      const uint32_t buf = lds0 + (uint32_t)((kBufs + (B + 2) % kBufs) * C::TILE);
+      if (!PAGED && j + 2 < n_full)
+        pp_copy_full<D>(src.v + (int64_t)(j + 2) * C::TILE, buf + wdst, voff);
+      else
+        pp_copy<D, PAGED>(src.v, src, (j + 2) * BN, pb.kv_len, buf, wave, lane, voff);
+    }
+    if (j < wt) {
+      const int n0 = j * BN;
+      const bool diag = CAUSAL ? (n0 + BN - 1 > pb.ctx + wq0) : false;
+      if (diag || n0 + BN > pb.kv_len) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);
+            const bool dead = (CAUSAL && key > qpos) || key >= pb.kv_len;
+            sc[kb][r] = dead ? kNegInf : sc[kb][r];
+          }
+      }
+      // max over this lane's 32 keys; the row max (both lane halves) is only
+      // needed when some lane's reference max must move
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleThreshold)) {
+        const float mt = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        const bool need = mt > m_run + kRescaleThreshold;
+        const float m_new = need ? mt : m_run;
+        const float alpha =
+            (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      // weights p = 2^(s*c - m): rounded to bf16 for the product with V,
+      // summed in fp32 (v_dot2 on the packed weights would be fewer
+      // instructions, but it cannot issue while the other wave's MFMAs
+      // occupy the matrix core; plain adds can)
+      const float mu = (m_run == kNegInf) ? 0.f : m_run;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, -mu));
+            pk[2 * kb + h][e] = (__bf16)pv;
+            part[e & 3] += pv;
+          }
+      l_run += (part[0] + part[1]) + (part[2] + part[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
+    }
+    phase_barrier();
+  };
+  static_assert(kBufs == 4, "the loop below is unrolled by kBufs");
+  for (int j = 0; j <= n; j += kBufs) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 > n) break;
+    step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 > n) break;
+    step(j + 2, std::integral_constant<int, 2>{});
+    if (j + 3 > n) break;
+    step(j + 3, std::integral_constant<int, 3>{});
+  }
+  if (grp == 0) phase_barrier();
+
+  // epilogue: o = O / l, lse = m*ln2 + ln(l)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int qrow = wq0 + lq;
+  if (qrow < pb.q_len) {
+    uint16_t* orow = pb.o + (int64_t)qrow * pb.row_stride;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 0] * inv));
+        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 1] * inv));
+        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 2] * inv));
+        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 3] * inv));
+        *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      }
+    if (pb.lse != nullptr && hf == 0)
+      pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
+  }
+}
+
 // Workgroup id -> logical work index. Consecutive workgroup ids are spread
 // round-robin over the 8 XCDs; this makes each XCD own a contiguous range of
 // logical work, so that query heads sharing K/V (and tiles of the same head)
@@ -406,9 +814,9 @@ __device__ __forceinline__ void logical_to_work(int logical, int units, int n_qt
   }
 }
 
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a, float c, int n_qt) {
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg<D, NW>::LDS];
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_kernel(PrefillArgs a, float c, int n_qt) {
+  __shared__ __attribute__((aligned(1024))) char lds[PP<D>::LDS];
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   int unit, qt;
   logical_to_work(logical, a.B * a.Hq, n_qt, unit, qt);
@@ -425,11 +833,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
   pb.q_len = a.T;
   pb.kv_len = a.T;
   pb.ctx = 0;
-  pb.m0 = qt * Cfg<D, NW>::BM;
+  pb.m0 = qt * kPPBM;
   KvSrc<false> src;
   src.k = (const char*)((const uint16_t*)a.k + kvoff);
   src.v = (const char*)((const uint16_t*)a.v + kvoff);
-  run_tile<D, NW, false, CAUSAL>(pb, src, c, lds);
+  run_pp<D, false, CAUSAL>(pb, src, c, lds);
 }
 
 // Paged prefill: sequences with q_len >= 2 of a paged batch (chunked prefill).
@@ -471,20 +879,19 @@ constexpr int kNW = 4;
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const float c = a.scale * kLog2e;
-  constexpr int BM = Cfg<128, kNW>::BM;
-  const int n_qt = (a.T + BM - 1) / BM;
+  const int n_qt = (a.T + kPPBM - 1) / kPPBM;
   const dim3 grid((unsigned)(n_qt * a.B * a.Hq));
-  const dim3 block(kNW * 64);
+  const dim3 block(kPPW * 64);
   if (a.d == 128) {
     if (a.causal)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, kNW, true>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_kernel<128, true>), grid, block, 0, s, a, c, n_qt);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, kNW, false>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_kernel<128, false>), grid, block, 0, s, a, c, n_qt);
   } else {
     if (a.causal)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, kNW, true>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_kernel<64, true>), grid, block, 0, s, a, c, n_qt);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, kNW, false>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_kernel<64, false>), grid, block, 0, s, a, c, n_qt);
   }
   return hipGetLastError();
 }
