@@ -237,7 +237,7 @@ def headline(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(
-                         "prefill_bf16_kernel<128,4,true> B=1 Hq=32 Hkv=8 T=16384")},
+                         "prefill_pp_kernel<128,true> B=1 Hq=32 Hkv=8 T=16384")},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": measured_traffic(
