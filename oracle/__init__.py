@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for fused causal attention and paged decode.
+"""CPU fp64 oracle for fused causal attention, paged decode and the paged
+cache append.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this package:
 only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
@@ -25,4 +26,5 @@ from .attention import (  # noqa: F401
     prefill,
     decode_paged,
     gather_paged_kv,
+    kv_append,
 )

@@ -175,3 +175,51 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale,
             o[t0:t1, h] = ob
             lse[t0:t1, h] = lb
     return o, lse
+
+
+def _raw(x):
+    """Element values as a numpy array, bit for bit (bf16 tensors through
+    their 16-bit patterns, which numpy has no float type for)."""
+    if hasattr(x, "detach"):
+        import torch  # local import: only needed for torch inputs
+
+        x = x.detach().to("cpu")
+        if x.dtype == torch.bfloat16:
+            x = x.view(torch.int16)
+        return x.numpy()
+    return np.asarray(x)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start_loc=None,
+              block_size=16):
+    """Paged caches after the new tokens' keys and values are written.
+
+    Definition ("Fast attention kernels and operator fusion", section
+    "FlashAttention-style attention and paged attention", second paragraph):
+    the cache grows by the new tokens; a paged cache holds keys and values in
+    fixed-size blocks and a block table maps every logical position to its
+    physical block. Sequence n's new rows qsl[n] .. qsl[n+1]-1 of k_new /
+    v_new ([num_tokens, Hkv, d]) are its last q_len positions L - q_len ..
+    L - 1 (L = seq_lens[n], which counts them); position t is slot
+    t % block_size of block block_table[n, t // block_size]. query_start_loc
+    None means one new row per sequence (row n).
+
+    Returns (k_cache, v_cache) as new numpy arrays holding the raw element
+    values (int16 bit patterns for bf16 tensors); the inputs are untouched.
+    """
+    kn, vn = _raw(k_new), _raw(v_new)
+    kc, vc = _raw(k_cache).copy(), _raw(v_cache).copy()
+    table = np.asarray(_raw(block_table), dtype=np.int64)
+    lens = np.asarray(_raw(seq_lens), dtype=np.int64)
+    num_seqs = lens.shape[0]
+    qsl = (np.arange(num_seqs + 1) if query_start_loc is None
+           else np.asarray(_raw(query_start_loc), dtype=np.int64))
+    for n in range(num_seqs):
+        t0, t1 = int(qsl[n]), int(qsl[n + 1])
+        q_len = t1 - t0
+        for i in range(q_len):
+            t = int(lens[n]) - q_len + i  # logical position of new row t0 + i
+            blk = int(table[n, t // block_size])
+            kc[blk, :, t % block_size, :] = kn[t0 + i]
+            vc[blk, :, t % block_size, :] = vn[t0 + i]
+    return kc, vc

@@ -339,3 +339,80 @@ def test_empty_sequence_gives_zero_and_minus_inf():
     np.testing.assert_array_equal(o[0], np.zeros_like(o[0]))
     assert np.all(lse[0] == -np.inf)
     assert np.all(np.isfinite(o[1]))
+
+
+# ---- paged cache append -------------------------------------------------
+
+def test_kv_append_hand_worked_golden():
+    # tests/golden/kv_append_hand.json: every write worked out by hand
+    cases = json.load(open(os.path.join(HERE, "golden", "kv_append_hand.json")))["cases"]
+    for c in cases:
+        shape = (c["num_blocks"], c["Hkv"], 16, c["d"])
+        k0, v0 = np.zeros(shape), np.zeros(shape)
+        qsl = c["query_start_loc"]
+        kc, vc = oracle.kv_append(np.array(c["k_new"], dtype=float),
+                                  np.array(c["v_new"], dtype=float), k0, v0,
+                                  np.array(c["block_table"]), np.array(c["seq_lens"]),
+                                  None if qsl is None else np.array(qsl))
+        ek, ev = np.zeros(shape), np.zeros(shape)
+        for w in c["writes"]:
+            ek[w["block"], w["head"], w["slot"]] = w["k"]
+            ev[w["block"], w["head"], w["slot"]] = w["v"]
+        assert np.array_equal(kc, ek), c["name"]
+        assert np.array_equal(vc, ev), c["name"]
+        assert not np.any(k0) and not np.any(v0)  # inputs untouched
+
+
+def test_kv_append_then_gather_returns_the_sequence():
+    # appending every token of a sequence (q_len = L) into a cache with a
+    # random table, then gathering positions 0..L-1, gives the rows back in
+    # order; the gather is the decode oracle's own, written separately
+    rng = np.random.default_rng(40)
+    for L in (1, 15, 16, 17, 50):
+        nb = -(-L // 16)
+        num_blocks = nb + 3
+        table = rng.permutation(num_blocks)[:nb].reshape(1, nb)
+        k_new = rng.standard_normal((L, 2, 4))
+        v_new = rng.standard_normal((L, 2, 4))
+        kc0 = rng.standard_normal((num_blocks, 2, 16, 4))
+        vc0 = rng.standard_normal((num_blocks, 2, 16, 4))
+        kc, vc = oracle.kv_append(k_new, v_new, kc0, vc0, table, np.array([L]), np.array([0, L]))
+        assert np.array_equal(oracle.gather_paged_kv(kc, table[0], L), k_new)
+        assert np.array_equal(oracle.gather_paged_kv(vc, table[0], L), v_new)
+
+
+def test_kv_append_touches_only_the_new_slots():
+    # slots other than the new tokens' keep their values (decode step after a
+    # chunk: positions written earlier are not disturbed)
+    rng = np.random.default_rng(41)
+    num_blocks, Hkv, d = 12, 2, 3
+    kc0 = rng.standard_normal((num_blocks, Hkv, 16, d))
+    vc0 = rng.standard_normal((num_blocks, Hkv, 16, d))
+    table = np.array([[4, 7, 1], [9, 0, 11]])
+    lens = np.array([40, 20])
+    qsl = np.array([0, 5, 6])  # 5 new rows for seq 0 (positions 35..39), 1 for seq 1 (19)
+    k_new = rng.standard_normal((6, Hkv, d))
+    v_new = rng.standard_normal((6, Hkv, d))
+    kc, vc = oracle.kv_append(k_new, v_new, kc0, vc0, table, lens, qsl)
+    written = {(1, s) for s in range(3, 8)} | {(0, 3)}  # (block, slot): 35..39 -> block 1, 19 -> block 0
+    for b in range(num_blocks):
+        for s in range(16):
+            if (b, s) not in written:
+                assert np.array_equal(kc[b, :, s], kc0[b, :, s]) and np.array_equal(vc[b, :, s], vc0[b, :, s])
+    assert np.array_equal(kc[1, :, 3:8], k_new[:5].transpose(1, 0, 2))
+    assert np.array_equal(vc[0, :, 3], v_new[5])
+
+
+def test_kv_append_keeps_bf16_bits():
+    # bf16 tensors are copied through their bit patterns, NaN payloads included
+    import torch
+
+    k_new = torch.tensor([[[1.5, -0.0]]], dtype=torch.bfloat16)
+    v_new = torch.tensor([[[float("nan"), 3.0]]], dtype=torch.bfloat16)
+    kc0 = torch.zeros(2, 1, 16, 2, dtype=torch.bfloat16)
+    kc, vc = oracle.kv_append(k_new, v_new, kc0, kc0.clone(), torch.tensor([[1]]),
+                              torch.tensor([3]))
+    assert kc.dtype == np.int16
+    assert list(kc[1, 0, 2]) == list(k_new.view(torch.int16).numpy()[0, 0])
+    assert list(vc[1, 0, 2]) == list(v_new.view(torch.int16).numpy()[0, 0])
+    assert not np.any(kc[0]) and not np.any(kc[1, 0, :2])

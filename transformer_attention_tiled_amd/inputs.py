@@ -163,6 +163,15 @@ def mixed_batch_inputs(n_chunks=8, chunk_len=512, n_decode=256, decode_len_range
                         seed=seed, device=device, poison=poison)
 
 
+def new_kv_rows(num_tokens, Hkv, d, seed, dtype=torch.bfloat16, device="cpu"):
+    """Keys and values of new tokens for a cache append: k_new, v_new
+    [num_tokens, Hkv, d], i.i.d. N(0,1) rounded to ``dtype`` (draw order k, v)."""
+    g = _gen(seed, device)
+    k = torch.randn(num_tokens, Hkv, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    v = torch.randn(num_tokens, Hkv, d, generator=g, device=device, dtype=torch.float32).to(dtype)
+    return k, v
+
+
 def compact_sequences(batch, seqs):
     """CPU copy of just the physical blocks that the given sequences use.
 
