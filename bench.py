@@ -317,6 +317,96 @@ def single(args, dev):
         return {"workload": w, "ms": round(ms, 4), "partition_size": PARTITION,
                 "chunk_gflop": round(fl / 1e9, 2),
                 "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
+    if w in ("append", "append_decode"):
+        # paged-cache append: "append" writes the mixed batch's new rows (8
+        # chunks x 512 + 256 decodes, Hkv=8, d=128) into its ~17.9 GB pool;
+        # "append_decode" one row per sequence of the 64-sequence decode batch
+        # (Hkv=2, d=128, lengths uniform in [256, 4096]), 8 rotated pools.
+        if w == "append":
+            pools = [inputs.mixed_batch_inputs(8, 512, 256, (1024, 32768), 32, 8, 128, seed=5,
+                                               device=dev)]
+            Hkv = 8
+        else:
+            pools = make_decode_sets(ROTATE, 64, 12, 2, 128, 256, 4096, 4, dev)
+            Hkv = 2
+        rows = [inputs.new_kv_rows(b["q"].shape[0], Hkv, 128, 105 + i, device=dev)
+                for i, b in enumerate(pools)]
+        with_qsl = w == "append"
+
+        def call(j):
+            b, (kn, vn) = pools[j], rows[j]
+            attn.kv_append(kn, vn, b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                           max_query_len=b["max_query_len"] if with_qsl else 1,
+                           query_start_loc=b["query_start_loc"] if with_qsl else None)
+        # the kernel is shorter than a Python-level call, so the calls are
+        # captured in a HIP graph (static addresses, one submission per
+        # replay) and the graph is replayed: the events then see GPU time
+        per_graph = 8 * len(pools) if len(pools) > 1 else 16
+        for j in range(len(pools)):
+            call(j)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(per_graph):
+                call(c % len(pools))
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(args.steps):
+            e = t.start()
+            graph.replay()
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms() / per_graph
+        nt = pools[0]["q"].shape[0]
+        by = 2 * (2 * nt * Hkv * 128 * 2)  # K and V rows, each read once and written once
+        return {"workload": w, "ms": round(ms, 5), "rows": nt, "bytes": by,
+                "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if w == "decode_step":
+        # one serving decode step on the 64-sequence batch (Hq=12, Hkv=2,
+        # d=128, lengths uniform in [256, 4096]): append the 64 new K/V rows
+        # to the paged cache, then paged attention; 8 rotated pools. Timed
+        # eagerly (events per step) and as a HIP graph of 8 steps (one per
+        # pool) replayed.
+        dsets = make_decode_sets(ROTATE, 64, 12, 2, 128, 256, 4096, 4, dev)
+        rows = [inputs.new_kv_rows(64, 2, 128, 105 + i, device=dev) for i in range(ROTATE)]
+
+        def step(j):
+            bd, (kn, vn) = dsets[j], rows[j]
+            attn.kv_append(kn, vn, bd["k_cache"], bd["v_cache"], bd["block_table"],
+                           bd["seq_lens"])
+            run_decode(bd)
+        for i in range(args.warmup):
+            step(i % ROTATE)
+        torch.cuda.synchronize()
+        t = Timer()
+        for i in range(args.steps):
+            e = t.start()
+            step(i % ROTATE)
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms_eager = t.mean_ms()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for j in range(ROTATE):
+                step(j)
+        for _ in range(max(1, args.warmup // ROTATE)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = Timer()
+        reps = max(1, args.steps // ROTATE)
+        for _ in range(reps):
+            e = t.start()
+            graph.replay()
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms_graph = t.mean_ms() / ROTATE
+        by = sum(decode_bytes(bd, 12, 2, 128) for bd in dsets) / ROTATE + 2 * (2 * 64 * 2 * 128 * 2)
+        return {"workload": w, "ms_eager": round(ms_eager, 5), "ms_graph": round(ms_graph, 5),
+                "bytes": by, "gbs_graph": round(by / (ms_graph * 1e-3) / 1e9, 1),
+                "frac_hbm_graph": round(by / (ms_graph * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     if w == "copy":
         # plain 1 GiB device-to-device copy: the calibration for the HBM byte
         # counters (what FETCH_SIZE / WRITE_SIZE read for a known size)
@@ -344,7 +434,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "c1", "c2", "c3", "c4", "c5", "copy"])
+                    choices=["headline", "c1", "c2", "c3", "c4", "c5", "append", "append_decode",
+                             "decode_step", "copy"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition length for decode (0: the library's choice)")
     args = ap.parse_args()

@@ -2,7 +2,8 @@
  * attn.h — C ABI of libattn.so: fused scaled-dot-product attention on AMD
  * Instinct MI355X (gfx950).
  *
- * Two operations, as the source pages state the problem:
+ * Two operations, as the source pages state the problem, and the cache
+ * append that feeds the second (attn_kv_append, below):
  *
  *  - attn_prefill: causal (or full) attention over contiguous Q, K, V,
  *    computed block by block so that the T x T score matrix never reaches
@@ -153,6 +154,43 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int max_query_len, int64_t num_blocks, float scale,
                       attn_dtype dtype, int partition_size, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_kv_append — write the new tokens' keys and values into a paged KV
+ * cache, the step before attn_decode_paged reads them. A paged cache keeps
+ * keys and values in fixed-size blocks and translates each logical position
+ * through a block table; the cache grows by the new tokens of every step
+ * ("Fast attention kernels and operator fusion", the-ai.news, section
+ * "FlashAttention-style attention and paged attention", second paragraph).
+ *
+ * Layout:
+ *   k_new, v_new : [num_tokens][Hkv][d] bf16, token-major (the rows of the
+ *                  new tokens, in the order of query_start_loc)
+ *   k_cache,
+ *   v_cache      : [num_blocks][Hkv][block_size][d] bf16, written in place
+ *   block_table, seq_lens, query_start_loc : exactly as in
+ *                  attn_decode_paged: sequence n owns rows qsl[n] ..
+ *                  qsl[n+1]-1 of k_new/v_new (q_len_n rows, NULL = one row
+ *                  per sequence, row n), which are its last positions
+ *                  L_n - q_len_n .. L_n - 1 (seq_lens counts them already).
+ * Effect: for every new row i of sequence n, at position t:
+ *   k_cache[block_table[n][t/16]][h][t%16][:] = k_new[i][h][:] for all h,
+ *   and the same for v. Nothing else in the caches is written.
+ * Preconditions not checked on the device: q_len_n <= L_n <= 16 *
+ * max_blocks_per_seq; the table entries of the written positions lie in
+ * [0, num_blocks); no two new rows
+ * map to the same cache slot (otherwise which one lands is unspecified).
+ * Supported: d in {64, 128}; dtype ATTN_BF16; block_size == 16. Pointers of
+ * k_new, v_new and the caches 16-byte aligned; the new rows must not overlap
+ * the caches. max_query_len >= every q_len_n (1 when query_start_loc is
+ * NULL).
+ * Returns ATTN_OK or a negative status; on error nothing is launched.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens,
+                   const int32_t* query_start_loc, int num_seqs, int num_tokens, int Hkv, int d,
+                   int block_size, int max_blocks_per_seq, int max_query_len, int64_t num_blocks,
+                   attn_dtype dtype, void* stream);
 
 /* attn_status_string — static, human-readable text for a status code. */
 const char* attn_status_string(int status);

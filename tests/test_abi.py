@@ -124,3 +124,27 @@ def test_workspace_size_and_partition_policy():
 def test_binding_raises_attn_error_with_code(lib):
     e = _binding.AttnError(SHAPE, "attn_prefill")
     assert e.status == SHAPE and "ATTN_ERR_SHAPE" in str(e)
+
+
+def append(lib, kn=P, vn=P2, kc=P3, vc=P4, table=P4 + 0x40000000, seq_lens=P4 + 0x40010000,
+           qsl=None, num_seqs=4, num_tokens=4, Hkv=2, d=128, block_size=16, mbps=8,
+           max_query_len=1, num_blocks=64, dtype=BF16):
+    return lib.attn_kv_append(kn, vn, kc, vc, table, seq_lens, qsl, num_seqs, num_tokens, Hkv, d,
+                              block_size, mbps, max_query_len, num_blocks, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), NULL), (dict(vn=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL),
+    (dict(table=None), NULL), (dict(seq_lens=None), NULL),
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(block_size=32), UNSUP),
+    (dict(num_seqs=0), SHAPE), (dict(num_tokens=0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(num_blocks=0), SHAPE), (dict(mbps=0), SHAPE), (dict(max_query_len=0), SHAPE),
+    (dict(max_query_len=2), SHAPE),             # several rows per sequence need query_start_loc
+    (dict(num_tokens=3), SHAPE),                # fewer rows than sequences
+    (dict(max_query_len=5, qsl=P4 + 0x40020000), SHAPE),  # bound above num_tokens
+    (dict(kn=P + 8), ALIGN), (dict(kc=P3 + 4), ALIGN), (dict(table=P4 + 0x40000002), ALIGN),
+    (dict(kn=P3), SHAPE),                       # new rows overlap the K cache
+    (dict(vc=P3 + 0x1000), SHAPE),              # the two caches overlap
+])
+def test_kv_append_rejects(lib, kw, code):
+    assert append(lib, **kw) == code

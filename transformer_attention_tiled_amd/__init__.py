@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     decode_paged,
     decode_paged_workspace_size,
     decode_paged_partition_size,
+    kv_append,
     status_string,
     library_path,
     load_library,

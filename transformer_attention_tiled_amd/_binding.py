@@ -72,6 +72,10 @@ def load_library():
                                       c_int, c_int, c_int, c_int, ctypes.c_int64, c_float,
                                       c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.attn_decode_paged.restype = c_int
+    lib.attn_kv_append.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   ctypes.c_int64, c_int, c_void_p]
+    lib.attn_kv_append.restype = c_int
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -164,3 +168,25 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, max
         _stream(q.device))
     _check(status, "attn_decode_paged")
     return o
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, *, max_query_len=1,
+              query_start_loc=None):
+    """attn_kv_append: write k_new / v_new [num_tokens,Hkv,d] into the paged
+    caches [num_blocks,Hkv,16,d] in place, at the positions block_table /
+    seq_lens / query_start_loc give (the convention of decode_paged).
+    ``max_query_len`` is a host-side bound on the new rows per sequence."""
+    lib = load_library()
+    num_tokens, Hkv, d = k_new.shape
+    num_blocks, _, block_size, _ = k_cache.shape
+    num_seqs = seq_lens.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("block_table", block_table)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    status = lib.attn_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(query_start_loc), num_seqs, num_tokens, Hkv, d, block_size,
+        block_table.shape[1], int(max_query_len), num_blocks, _dtype_code(k_new.dtype),
+        _stream(k_new.device))
+    _check(status, "attn_kv_append")

@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 OUT = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip"]
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
+           "kv_append.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -178,4 +178,41 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   return ATTN_OK;
 }
 
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens,
+                   const int32_t* query_start_loc, int num_seqs, int num_tokens, int Hkv, int d,
+                   int block_size, int max_blocks_per_seq, int max_query_len, int64_t num_blocks,
+                   attn_dtype dtype, void* stream) {
+  if (k_new == nullptr || v_new == nullptr || k_cache == nullptr || v_cache == nullptr ||
+      block_table == nullptr || seq_lens == nullptr)
+    return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || num_tokens < 1 || Hkv < 1 || num_blocks < 1 || max_blocks_per_seq < 1 ||
+      max_query_len < 1 || max_query_len > num_tokens)
+    return ATTN_ERR_SHAPE;
+  if (!supported_d(d) || block_size != attn::kBlockSize) return ATTN_ERR_UNSUPPORTED;
+  if (query_start_loc == nullptr && (max_query_len != 1 || num_tokens < num_seqs))
+    return ATTN_ERR_SHAPE;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(query_start_loc, 4))
+    return ATTN_ERR_ALIGN;
+  const int64_t nbytes = (int64_t)num_tokens * Hkv * d * 2;
+  const int64_t cbytes = num_blocks * Hkv * attn::kBlockSize * d * 2;
+  if (overlap(k_cache, cbytes, v_cache, cbytes) || overlap(k_new, nbytes, k_cache, cbytes) ||
+      overlap(k_new, nbytes, v_cache, cbytes) || overlap(v_new, nbytes, k_cache, cbytes) ||
+      overlap(v_new, nbytes, v_cache, cbytes))
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)attn::append_grid(num_tokens) > kMaxGrid) return ATTN_ERR_SHAPE;
+
+  attn::AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.qsl = query_start_loc;
+  a.num_seqs = num_seqs; a.num_tokens = num_tokens; a.Hkv = Hkv; a.d = d;
+  a.max_blocks_per_seq = max_blocks_per_seq; a.max_query_len = max_query_len;
+  if (attn::launch_kv_append_bf16(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_LAUNCH;
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -40,6 +40,20 @@ struct PagedArgs {
   float* ws_lse;       // split-KV partial log2-sum-exp [num_seqs][Hq][max_parts]
 };
 
+// Append to a paged cache: k_new,v_new [num_tokens][Hkv][d] written into
+// caches [num_blocks][Hkv][16][d] at the positions the block table gives.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;  // [num_seqs][max_blocks_per_seq]
+  const int32_t* seq_lens;     // [num_seqs]
+  const int32_t* qsl;          // [num_seqs + 1] or nullptr (one new token per sequence)
+  int num_seqs, num_tokens, Hkv, d;
+  int max_blocks_per_seq, max_query_len;
+};
+
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;  // tokens per split-KV partition, at most
 
@@ -50,5 +64,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s);  // q_len >= 2 sequences
 hipError_t launch_paged_decode_bf16(const PagedArgs& a, hipStream_t s);   // q_len == 1 sequences
+int append_grid(int num_tokens);  // workgroups of the append launch
+hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t s);
 
 }  // namespace attn

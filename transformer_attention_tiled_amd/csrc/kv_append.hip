@@ -1,0 +1,137 @@
+// Append of the new tokens' keys and values to a paged KV cache, bf16.
+//
+// The cache keeps the keys and values computed so far and grows by one
+// token's worth per generated token; a paged cache stores them in fixed-size
+// blocks and a block table maps each logical position to its physical block
+// ("Fast attention kernels and operator fusion", the-ai.news, section
+// "FlashAttention-style attention and paged attention", second paragraph).
+// This kernel is the write side of that translation: the new token at
+// logical position t of sequence n goes to slot t % 16 of physical block
+// block_table[n][t / 16].
+//
+// Token convention (the one attn_decode_paged reads back): sequence n owns
+// rows qsl[n] .. qsl[n+1]-1 of k_new / v_new, which are its last q_len
+// positions L - q_len .. L - 1 (L = seq_lens[n] counts them already).
+//
+// Work decomposition: workgroup = kRun consecutive rows of k_new / v_new
+// (every workgroup has work), 256 threads, each moving 16-byte chunks. A
+// token's K (or V) row is Hkv head rows of d contiguous elements in the
+// source and Hkv rows of the same length, block_size * d elements apart, in
+// the cache block; consecutive threads take consecutive chunks, so every
+// head row is read and written as whole 128-byte lines. The loads of the
+// new rows depend on nothing and are issued first; meanwhile the workgroup
+// finds each row's sequence (binary search over query_start_loc, staged in
+// LDS), position and physical block, then issues the stores. Each byte is
+// read once and written once: the kernel is bound by HBM bandwidth and
+// latency (it does no arithmetic).
+#include <hip/hip_runtime.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRun = 8;        // rows of k_new / v_new per workgroup
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;     // 16-byte moves in flight per thread and round
+constexpr int kQslLds = 4096;  // query_start_loc entries staged in LDS, at most
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
+  __shared__ int qsl_s[kQslLds];
+  __shared__ int64_t row_base[kRun];  // cache element offset of each row's (block, slot), head 0
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * kRun;
+  const int nt = min(kRun, a.num_tokens - r0);
+  constexpr int CH = D / 8;          // 16-byte chunks per head row
+  const int per_tok = a.Hkv * CH;    // chunks per row, per matrix
+  const int per_mat = nt * per_tok;  // chunks of the workgroup, per matrix
+  const int rounds = (2 * per_mat + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const uint16_t* src_k = (const uint16_t*)a.k_new + (int64_t)r0 * a.Hkv * D;
+  const uint16_t* src_v = (const uint16_t*)a.v_new + (int64_t)r0 * a.Hkv * D;
+  uint16_t* const kc = (uint16_t*)a.k_cache;
+  uint16_t* const vc = (uint16_t*)a.v_cache;
+
+  // first round of loads: independent of everything below
+  u32x4 val[kUnroll];
+  auto load_round = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < 2 * per_mat) {
+        const bool is_v = x >= per_mat;
+        const int r = is_v ? x - per_mat : x;  // (row, head, chunk) of the workgroup
+        val[u] = *(const u32x4*)((is_v ? src_v : src_k) + (int64_t)r * 8);
+      }
+    }
+  };
+  load_round(0);
+
+  // each row's sequence n, position and physical block
+  const bool staged = a.qsl != nullptr && a.num_seqs < kQslLds;
+  if (staged)
+    for (int i = tid; i <= a.num_seqs; i += kThreads) qsl_s[i] = a.qsl[i];
+  __syncthreads();
+  if (tid < nt) {
+    const int t = r0 + tid;  // row of k_new / v_new
+    const int rows = a.qsl != nullptr ? (staged ? qsl_s[a.num_seqs] : a.qsl[a.num_seqs])
+                                      : a.num_seqs;
+    row_base[tid] = -1;  // a row past the last sequence's rows is not written
+    if (t < rows) {
+      int n = t;
+      if (a.qsl != nullptr) {
+        // largest n with qsl[n] <= t (sequences without rows have qsl[n] == qsl[n+1])
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          const int q = staged ? qsl_s[mid] : a.qsl[mid];
+          if (q <= t) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+      }
+      const int t0 = a.qsl != nullptr ? (staged ? qsl_s[n] : a.qsl[n]) : n;
+      const int t1 = a.qsl != nullptr ? (staged ? qsl_s[n + 1] : a.qsl[n + 1]) : n + 1;
+      const int pos = a.seq_lens[n] - (t1 - t0) + (t - t0);
+      const int64_t blk = a.block_table[(int64_t)n * a.max_blocks_per_seq + (pos >> 4)];
+      row_base[tid] = (blk * a.Hkv * kBlockSize + (pos & 15)) * D;
+    }
+  }
+  __syncthreads();
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int base = rd * kThreads * kUnroll;
+    if (rd > 0) load_round(base);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < 2 * per_mat) {
+        const bool is_v = x >= per_mat;
+        const int r = is_v ? x - per_mat : x;
+        const int ti = r / per_tok;
+        const int gc = r - ti * per_tok;  // head * CH + chunk
+        const int g = gc / CH;
+        const int64_t rb = row_base[ti];
+        if (rb >= 0)
+          *(u32x4*)((is_v ? vc : kc) + rb + (int64_t)g * (kBlockSize - 1) * D + (int64_t)gc * 8) =
+              val[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int append_grid(int num_tokens) { return (num_tokens + kRun - 1) / kRun; }
+
+hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)append_grid(a.num_tokens));
+  if (a.d == 128)
+    hipLaunchKernelGGL((kv_append_kernel<128>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<64>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn
