@@ -291,13 +291,18 @@ def single(args, dev):
         return {"workload": w, "ms": round(ms, 5), "gbs": round(gbs, 1),
                 "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "partition_size": PARTITION or
                 attn.decode_paged_partition_size(64, 2, max(bd["max_seq_len"] for bd in dsets))}
-    if w == "c5":
-        # 8 chunks of 512 new tokens (no prior context) + 256 decodes,
-        # lengths uniform in [1024, 32768]; one shuffled pool on the GPU.
+    if w in ("c5", "c5ctx"):
+        # 8 chunks of 512 new tokens + 256 decodes, lengths uniform in
+        # [1024, 32768]; one shuffled pool on the GPU. c5: the chunks have no
+        # prior context; c5ctx: each chunk's sequence is also 1024..32768
+        # long, so it follows L - 512 cached tokens.
         n_chunks, n_dec = 8, 256
-        b = inputs.mixed_batch_inputs(n_chunks, 512, n_dec, (1024, 32768), 32, 8, 128, seed=5,
-                                      device=dev)
+        ctx = w == "c5ctx"
+        b = inputs.mixed_batch_inputs(n_chunks, 512, n_dec, (1024, 32768), 32, 8, 128,
+                                      seed=7 if ctx else 5, device=dev,
+                                      chunk_len_range=(1024, 32768) if ctx else None)
         dec_lens = b["seq_lens_host"][n_chunks:]
+        chunk_lens = b["seq_lens_host"][:n_chunks]
         b["o"] = torch.empty_like(b["q"])
         b["ws"] = torch.empty(attn.decode_paged_workspace_size(
             n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8,
@@ -312,8 +317,9 @@ def single(args, dev):
             t.stop(e)
         torch.cuda.synchronize()
         ms = t.mean_ms()
-        fl = n_chunks * causal_flops(1, 32, 512, 128)
-        kv = sum(dec_lens) * 8 * 128 * 2 * 2 + n_chunks * 512 * 8 * 128 * 2 * 2
+        # chunk flops: row i of a chunk after c cached tokens sees c + i + 1 keys
+        fl = sum(4.0 * 32 * 128 * (512 * (L - 512) + 512 * 513 / 2) for L in chunk_lens)
+        kv = (sum(dec_lens) + sum(chunk_lens)) * 8 * 128 * 2 * 2
         return {"workload": w, "ms": round(ms, 4), "partition_size": PARTITION,
                 "chunk_gflop": round(fl / 1e9, 2),
                 "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
@@ -434,8 +440,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "c1", "c2", "c3", "c4", "c5", "append", "append_decode",
-                             "decode_step", "copy"])
+                    choices=["headline", "c1", "c2", "c3", "c4", "c5", "c5ctx", "append",
+                             "append_decode", "decode_step", "copy"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition length for decode (0: the library's choice)")
     args = ap.parse_args()

@@ -75,6 +75,29 @@ def test_chunk_rows_match_contiguous_prefill():
     assert (a - c).abs().max().item() <= 2e-2
 
 
+def test_mixed_many_sequences_direct_grid():
+    # more sequences than the persistent chunk kernel stages (2048): the chunk
+    # path then launches one workgroup per (query tile, sequence, head) of the
+    # host bound, and workgroups of single-token sequences exit at once
+    print("[mixed] 2100 sequences, chunks every 100th", flush=True)
+    rng = np.random.default_rng(73)
+    q_lens = [1] * 2100
+    for n in range(0, 2100, 100):
+        q_lens[n] = int(rng.integers(2, 300))
+    seq_lens = [q + int(rng.integers(0, 200)) for q in q_lens]
+    b = inputs.paged_inputs(2100, 4, 2, 64, seq_lens=seq_lens, q_lens=q_lens, seed=73)
+    o, lse = run(b)
+    chunks = list(range(0, 2100, 100))
+    dec = sorted(set(int(x) for x in rng.choice(2100, 40, replace=False)) - set(chunks))
+    seqs = chunks + dec
+    kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
+    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, 1.0 / math.sqrt(64), query_start_loc=qsl_c)
+    qsl = b["query_start_loc"]
+    rows = torch.cat([torch.arange(int(qsl[n]), int(qsl[n + 1])) for n in seqs])
+    assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "2100 sequences")
+    assert_lse_close(lse[rows.to(DEV)], rl, "2100 sequences")
+
+
 def test_config_mixed_batch_full_size_sampled():
     # 8 chunks of 512 new tokens + 256 decodes with lengths uniform in
     # [1024, 32768], Hq=32, Hkv=8, d=128, one shuffled pool (~17.9 GB) drawn
@@ -100,5 +123,53 @@ def test_config_mixed_batch_full_size_sampled():
     rows = torch.cat([torch.arange(int(qsl_full[n]), int(qsl_full[n + 1])) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "full-size mixed")
     assert_lse_close(lse[rows.to(DEV)], rl, "full-size mixed")
+    del b
+    torch.cuda.empty_cache()
+
+
+def test_config_mixed_batch_with_context_full_size_sampled():
+    # the mixed batch with prior context: 8 chunks of 512 new tokens whose
+    # sequences are 1024..32768 long (so each chunk follows up to 32256 cached
+    # tokens), next to 256 decodes, Hq=32, Hkv=8, d=128, one shuffled pool on
+    # the GPU, in the launch configuration the benchmark times. The oracle
+    # checks 8 rows of every chunk (first, last, the rest seeded) against the
+    # contiguous causal prefill of the gathered sequence at those rows, and 16
+    # decode sequences including the shortest and longest.
+    print("[mixed] full-size batch with context", flush=True)
+    b = inputs.mixed_batch_inputs(8, 512, 256, (1024, 32768), 32, 8, 128, seed=7, device=DEV,
+                                  chunk_len_range=(1024, 32768))
+    o = torch.empty_like(b["q"])
+    lse = torch.full(tuple(b["q"].shape[:2]), float("nan"), device=DEV)
+    attn.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                      max_seq_len=b["max_seq_len"], max_query_len=b["max_query_len"],
+                      query_start_loc=b["query_start_loc"], o=o, lse=lse)
+    torch.cuda.synchronize()
+    lens = b["seq_lens_host"]
+    qsl = b["query_start_loc"].cpu()
+    rng = np.random.default_rng(7)
+    scale = 1.0 / math.sqrt(128)
+    for n in range(8):
+        L = lens[n]
+        ctx = L - 512
+        picks = sorted({0, 511} | set(int(x) for x in rng.choice(512, 6, replace=False)))
+        kc, vc, table, sl, q, _ = inputs.compact_sequences(b, [n])
+        K = oracle.gather_paged_kv(kc, table[0].numpy(), L).transpose(1, 0, 2)[None]
+        V = oracle.gather_paged_kv(vc, table[0].numpy(), L).transpose(1, 0, 2)[None]
+        Q = np.zeros((1, 32, L, 128))
+        Q[0, :, ctx:] = q.double().numpy().transpose(1, 0, 2)
+        ro, rl = oracle.prefill(Q, K, V, scale, causal=True, rows=[ctx + i for i in picks])
+        rows = torch.tensor([int(qsl[n]) + i for i in picks])
+        got = o[rows.to(DEV)].transpose(0, 1)  # [Hq, rows, d]
+        assert_close(got, ro[0], torch.bfloat16, f"chunk {n} (context {ctx})")
+        assert_lse_close(lse[rows.to(DEV)].transpose(0, 1), rl[0], f"chunk {n} lse")
+    dec = list(range(8, 264))
+    pick = {min(dec, key=lambda n: lens[n]), max(dec, key=lambda n: lens[n])}
+    pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
+    seqs = sorted(pick)
+    kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
+    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, scale, query_start_loc=qsl_c)
+    rows = torch.tensor([int(qsl[n]) for n in seqs])
+    assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "decodes next to context chunks")
+    assert_lse_close(lse[rows.to(DEV)], rl, "decodes next to context chunks")
     del b
     torch.cuda.empty_cache()

@@ -62,6 +62,25 @@ bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partit
 
 }  // namespace
 
+namespace attn {
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};  // 0: not queried yet (same value if two threads race)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+}  // namespace attn
+
 extern "C" {
 
 const char* attn_status_string(int status) {
@@ -157,7 +176,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
   if ((int64_t)w.max_parts * Hkv * num_seqs > kMaxGrid) return ATTN_ERR_SHAPE;
-  const int64_t n_qt = ((int64_t)max_query_len + 127) / 128;
+  const int64_t n_qt = ((int64_t)max_query_len + 255) / 256;  // 256-row query tiles
   if (n_qt * num_seqs * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
 
   attn::PagedArgs a;

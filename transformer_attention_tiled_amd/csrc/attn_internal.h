@@ -57,6 +57,9 @@ struct AppendArgs {
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;  // tokens per split-KV partition, at most
 
+// Compute units of the current device (queried once per device and cached).
+int device_cu_count();
+
 // Host-side policy shared by the workspace query and the launch.
 int decode_partition_size(int num_seqs, int Hkv, int max_seq_len);
 

@@ -10,31 +10,26 @@
 // attention profiling guide", aiexpert.news, second paragraph) up to
 // rounding order.
 //
-// Work decomposition
-//   workgroup  = NW waves = (batch b | sequence n, query head h, tile of
-//                BM = 32*NW query rows); K/V head = h / (Hq/Hkv).
+// Work decomposition (details with the two-group schedule below)
+//   workgroup  = 8 waves = (batch b | sequence n, query head h, tile of 256
+//                query rows); K/V head = h / (Hq/Hkv).
 //   key tile   = BN = 64 keys. K and V tiles are copied from HBM straight
 //                into LDS (global_load_lds_dwordx4: each instruction moves
-//                one contiguous KiB, lane L's 16 bytes to M0 + 16 L), double
-//                buffered: the copies of tile j+1 are in flight while tile j
-//                is computed. Each lane's source offsets are fixed for the
-//                whole loop and the tile base is a scalar, so the copies cost
-//                no vector ALU work; only the ragged last tile clamps its
-//                rows to the last key.
+//                one contiguous KiB, lane L's 16 bytes to M0 + 16 L), into
+//                four buffers each, three tiles ahead. Each lane's source
+//                offsets are fixed for the whole loop and the tile base is a
+//                scalar (for a paged cache: the block's table entry, read
+//                ahead with a scalar load), so the copies cost no vector ALU
+//                work; only the ragged last tile clamps its rows to the last
+//                key.
 //   wave       = 32 query rows. The wave computes the TRANSPOSED scores
 //                S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that each lane
 //                owns one query column: the row max and row sum of the
 //                softmax are in-lane reductions plus one exchange with the
 //                lane 32 apart. O^T = V^T P^T is the second MFMA chain; P^T
 //                is fed straight from the S^T accumulators (rounded to bf16).
-//
-// Why vector ALU work is the budget: on this chip VALU instructions do not
-// hide behind MFMA (issue is shared), so every VALU instruction per tile
-// costs MFMA throughput. The tile loop therefore keeps only the softmax on
-// the VALU: copies are DMA, the V^T operand comes from the LDS transpose
-// read ds_read_b64_tr_b16, and row sums use v_dot2_f32_bf16 on the packed
-// bf16 weights (two per instruction; summing the rounded weights also makes
-// the weights that multiply V sum exactly to the normaliser).
+//                The V^T operand comes from the LDS transpose read
+//                ds_read_b64_tr_b16. Row sums add the unrounded fp32 weights.
 //
 // MFMA 32x32x16 bf16 operand layout (checked on gfx950): lane l holds
 //   A[i = l%32][k = 8*(l/32) + e], B[k = 8*(l/32) + e][j = l%32], e = 0..7,
@@ -51,10 +46,10 @@
 // d0 + 4*(i%4), lane j receives V[K0..K0+3][d0 + j]: four consecutive keys
 // of one d column. Two such reads give the 8 keys of one V^T operand.
 //
-// LDS layout: K and V tiles row-major (one key per row), 16-byte chunks
-// XOR-swizzled per row with f(r) = 4*(r%4) + (r/4)%4, which spreads both the
-// K operand reads (16 rows, same chunk) and the transpose reads (4 rows, 4
-// adjacent chunks) over the banks.
+// LDS layout: K and V tiles row-major (one key per row). K tiles have their
+// 16-byte chunks XOR-swizzled per row with f(r) = 4*(r%4) + (r/4)%4, which
+// spreads the K operand reads (16 rows, same chunk) over the banks; V tiles
+// have their own swizzle for the transpose reads (below).
 //
 // Online softmax (the pages say "updates the softmax statistics"; the
 // recurrence here is the standard running max / running sum): scores are
@@ -71,6 +66,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -79,7 +76,6 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -91,20 +87,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kNegInf = -__builtin_inff();
-
-template <int D, int NW>
-struct Cfg {
-  static constexpr int NT = NW * 64;           // threads
-  static constexpr int BM = NW * 32;           // query rows per workgroup
-  static constexpr int ROW = D * 2;            // bytes per key row in LDS
-  static constexpr int NCH = D / 8;            // 16-byte chunks per row
-  static constexpr int TILE = BN * ROW;        // bytes of a K (or V) tile
-  static constexpr int STAGE = 2 * TILE;       // K tile then V tile
-  static constexpr int LDS = 2 * STAGE;        // double buffered
-  static constexpr int COPIES = TILE / 1024 / NW;  // KiB copies per wave per tile
-  static constexpr int RPC = 1024 / ROW;       // rows per KiB copy
-  static_assert(COPIES >= 1 && TILE % (1024 * NW) == 0, "tile copy split");
-};
 
 __device__ __forceinline__ int swz(int r, int nch) { return (4 * (r & 3) + ((r >> 2) & 3)) & (nch - 1); }
 
@@ -124,7 +106,6 @@ __device__ __forceinline__ void copy_vaddr(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds), "v"(src) : "memory", "m0");
 }
-__device__ __forceinline__ void wait_all_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Where a workgroup's K/V rows live.
 template <bool PAGED>
@@ -156,231 +137,6 @@ struct Problem {
   int ctx;            // absolute position of query row 0 (query i sees keys <= ctx + i)
   int m0;             // first query row of this workgroup
 };
-
-// Copies of key tile n0 into LDS stage `stage` (LDS address). Every wave
-// copies COPIES KiB of K and of V. Rows past the last key re-read the last
-// key's row (never storage past the sequence); those keys are masked.
-template <int D, int NW, bool PAGED>
-__device__ __forceinline__ void copy_tile(const KvSrc<PAGED>& src, int n0, int kv_len,
-                                          uint32_t stage, int wave, int lane,
-                                          const uint32_t* off) {
-  using C = Cfg<D, NW>;
-  const bool full = n0 + BN <= kv_len;
-#pragma unroll
-  for (int s = 0; s < C::COPIES; ++s) {
-    const uint32_t lk = stage + (wave * C::COPIES + s) * 1024;
-    const uint32_t lv = lk + C::TILE;
-    const int t = (wave * C::COPIES + s) * C::RPC + lane / (C::ROW / 16);  // tile row
-    if constexpr (!PAGED) {
-      if (full) {
-        copy_saddr(src.k + (int64_t)n0 * C::ROW, off[s], lk);
-        copy_saddr(src.v + (int64_t)n0 * C::ROW, off[s], lv);
-      } else {
-        const int tc = min(t, kv_len - 1 - n0);
-        const uint32_t o = off[s] + (uint32_t)((tc - t) * C::ROW);
-        copy_saddr(src.k + (int64_t)n0 * C::ROW, o, lk);
-        copy_saddr(src.v + (int64_t)n0 * C::ROW, o, lv);
-      }
-    } else {
-      const int key = min(n0 + t, kv_len - 1);
-      const int64_t row = (int64_t)src.table[key >> 4] * src.block_bytes + (key & 15) * C::ROW;
-      const uint32_t inrow = off[s] - (uint32_t)(t * C::ROW);  // chunk byte offset
-      copy_vaddr(src.k + row + inrow, lk);
-      copy_vaddr(src.v + row + inrow, lv);
-    }
-  }
-}
-
-template <int D, int NW, bool PAGED, bool CAUSAL>
-__device__ __forceinline__ void run_tile(const Problem& pb, const KvSrc<PAGED>& src, float c,
-                                         char* lds) {
-  using C = Cfg<D, NW>;
-  const int tid = threadIdx.x;
-  // the wave index is the same in every lane: say so, so that everything
-  // derived from it (copy destinations, tile bounds) stays in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int lq = lane & 31;  // query column owned by this lane
-  const int hf = lane >> 5;  // which half of the key rows
-
-  // key range of the workgroup and of this wave
-  const int wg_last_q = min(pb.m0 + C::BM, pb.q_len);  // exclusive
-  const int wg_keys = CAUSAL ? min(pb.kv_len, pb.ctx + wg_last_q) : pb.kv_len;
-  const int n_tiles = (wg_keys + BN - 1) / BN;
-  const int wq0 = pb.m0 + wave * 32;
-  const int w_last_q = min(wq0 + 32, pb.q_len);
-  const int w_keys = wq0 >= pb.q_len ? 0 : (CAUSAL ? min(pb.kv_len, pb.ctx + w_last_q) : pb.kv_len);
-  const int w_tiles = (w_keys + BN - 1) / BN;
-
-  // per-lane source byte offsets of the tile copies (tile-relative)
-  uint32_t off[C::COPIES];
-#pragma unroll
-  for (int s = 0; s < C::COPIES; ++s) {
-    const int lds_off = (wave * C::COPIES + s) * 1024 + 16 * lane;
-    const int t = lds_off / C::ROW;
-    const int pc = (lds_off % C::ROW) / 16;
-    off[s] = (uint32_t)(t * C::ROW + ((pc ^ swz(t, C::NCH)) * 16));
-  }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-
-  if (n_tiles > 0) copy_tile<D, NW, PAGED>(src, 0, pb.kv_len, lds0, wave, lane, off);
-
-  // Q^T fragments: B operand, lane holds Q[wq0 + lq][16*s + 8*hf + e]
-  bf16x8 qf[D / 16];
-  {
-    const int qrow = min(wq0 + lq, pb.q_len - 1);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[s] = __builtin_bit_cast(
-          bf16x8, *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf));
-  }
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;  // reference max, log2 units
-  float l_run = 0.f;      // partial row sum over this lane's keys
-  const int qpos = pb.ctx + wq0 + lq;  // absolute position of this lane's query
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // K operand rows of the two 32-key blocks (sigma order) and the lane's
-  // position in its group of 16 for the transpose reads
-  const int krow0 = sigma32(lq);
-  const int g16 = lane >> 4, i16 = lane & 15;
-
-  // Q landed and the first tile's copies are done everywhere.
-  __builtin_amdgcn_s_waitcnt(0);
-  wait_all_copies();
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int n0 = j * BN;
-    const uint32_t cur = lds0 + (j & 1) * C::STAGE;
-    if (j + 1 < n_tiles)
-      copy_tile<D, NW, PAGED>(src, n0 + BN, pb.kv_len, lds0 + ((j + 1) & 1) * C::STAGE, wave,
-                              lane, off);
-
-    if (j < w_tiles) {
-      const lds_char* sk = (const lds_char*)(uintptr_t)cur;
-      const lds_char* sv = sk + C::TILE;
-      // S^T = K Q^T for 2 blocks of 32 keys
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int r = 32 * kb + krow0;
-        const lds_char* kp = sk + r * C::ROW;
-        const int sw = swz(r, C::NCH);
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          const bf16x8 a = *(const bf16x8 __attribute__((address_space(3)))*)(
-              kp + (((2 * st + hf) ^ sw) * 16));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-        }
-      }
-      // mask keys after the query (causal) and keys past the end
-      const bool diag = CAUSAL ? (n0 + BN - 1 > pb.ctx + wq0) : false;
-      if (diag || n0 + BN > pb.kv_len) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);
-            const bool dead = (CAUSAL && key > qpos) || key >= pb.kv_len;
-            s[kb][r] = dead ? kNegInf : s[kb][r];
-          }
-      }
-      // tile row max (raw scores), shared by the two lane halves
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * c;
-      const bool need = mt > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        // lanes that do not need it keep m and scale by 1, so a row's result
-        // never depends on the other rows of the wave
-        const float m_new = need ? fmaxf(m_run, mt) : m_run;
-        const float alpha =
-            (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-      const float mu = (m_run == kNegInf) ? 0.f : m_run;
-      // weights p = 2^(s*c - m) rounded to bf16, and their sum
-      bf16x8 pk[4];
-      float part[2] = {0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pk[2 * kb + h][e] =
-                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * h + e], c, -mu));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pp = {pk[2 * kb + h][e], pk[2 * kb + h][e + 1]};
-            part[h] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, part[h], false);
-          }
-        }
-      l_run += part[0] + part[1];
-      // O^T += V^T P^T; V^T operand: two transpose reads of 4 keys each
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          u32x2 half[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row = 16 * kk + 8 * (g16 >> 1) + 4 * hh + (i16 >> 2);
-            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);  // element
-            const lds_char* p =
-                sv + row * C::ROW + ((((col >> 3) ^ swz(row, C::NCH)) * 16) + (col & 7) * 2);
-            half[hh] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (s16x4 __attribute__((address_space(3)))*)p));
-          }
-          const u32x4 both = {half[0][0], half[0][1], half[1][0], half[1][1]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
-                                                            pk[kk], acc[db], 0, 0, 0);
-        }
-      }
-    }
-
-    // this wave's copies of tile j+1 have landed; after the barrier every
-    // wave's have, and nobody reads tile j any more
-    wait_all_copies();
-    __syncthreads();
-  }
-
-  // epilogue: o = O / l, lse = m*ln2 + ln(l)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int qrow = wq0 + lq;
-  if (qrow < pb.q_len) {
-    uint16_t* orow = pb.o + (int64_t)qrow * pb.row_stride;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 0] * inv));
-        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 1] * inv));
-        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 2] * inv));
-        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 3] * inv));
-        *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-      }
-    if (pb.lse != nullptr && hf == 0)
-      pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Two-group schedule. On gfx950 the vector ALU work of one wave runs alongside
@@ -480,6 +236,25 @@ __device__ __forceinline__ void pp_copy_full(const char* tile, uint32_t dst, con
   using C = PP<D>;
 #pragma unroll
   for (int s = 0; s < C::CP; ++s) copy_saddr(tile, off[s], dst + s * 1024);
+}
+
+// Steady-state copy of a full tile through the block table. The RPC rows of
+// one KiB copy instruction are consecutive keys inside one 16-key block, so
+// the instruction needs one table entry, the same for the whole wave:
+// `blk[s]`, read ahead of time with a scalar load. `dst` is this wave's first
+// KiB in the LDS buffer.
+template <int D>
+__device__ __forceinline__ void pp_copy_paged(const char* base, int64_t block_bytes,
+                                              const int* blk, int n0, uint32_t dst, int wave,
+                                              const uint32_t* off) {
+  using C = PP<D>;
+  static_assert(kBlockSize % C::RPC == 0, "a copy instruction stays inside one block");
+#pragma unroll
+  for (int s = 0; s < C::CP; ++s) {
+    const int tb = (wave * C::CP + s) * C::RPC;  // first tile row of copy s
+    const char* row = base + (int64_t)blk[s] * block_bytes + ((n0 + tb) & 15) * C::ROW;
+    copy_saddr(row, off[s] - (uint32_t)(tb * C::ROW), dst + s * 1024);
+  }
 }
 
 // M phase: O^T += V^T P^T over the previous tile (16 MFMAs at D = 128), then
@@ -651,6 +426,28 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   float m_run = kNegInf;  // reference max, log2 units
   float l_run = 0.f;      // partial row sum over this lane's keys
   const int qpos = pb.ctx + wq0 + lq;
+  // Paged: the table entries of this wave's copy rows, read with scalar loads
+  // one step before use (the copies of K tile t in S(t-3) and of V tile t in
+  // S(t-2) need the same entries): ev for the V copy of this step, ek for the
+  // K copy. Reads past the sequence are clamped to its last key.
+  int ek[C::CP], ev[C::CP];
+  auto table_row = [&](int tile, int s) -> int {
+    if constexpr (PAGED) {
+      const __attribute__((address_space(4))) int32_t* t4 =
+          (const __attribute__((address_space(4))) int32_t*)src.table;
+      const int key = min(tile * BN + (wave * C::CP + s) * C::RPC, pb.kv_len - 1);
+      return t4[key >> 4];
+    } else {
+      return 0;
+    }
+  };
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int s = 0; s < C::CP; ++s) {
+      ev[s] = table_row(2, s);
+      ek[s] = table_row(3, s);
+    }
+  }
 
   // Both groups run the same sequence M(j), barrier, S(j), barrier; group 1
   // starts one barrier later (and group 0 ends with one), which puts the two
@@ -686,17 +483,32 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
     // before the previous barrier), then mask, running max, weights, sums.
     if (j + 3 < n) {
       const uint32_t buf = lds0 + (uint32_t)(((B + 3) % kBufs) * C::TILE);
-      if (!PAGED && j + 3 < n_full)
-        pp_copy_full<D>(src.k + (int64_t)(j + 3) * C::TILE, buf + wdst, koff);
-      else
+      if (j + 3 < n_full) {
+        if constexpr (PAGED)
+          pp_copy_paged<D>(src.k, src.block_bytes, ek, (j + 3) * BN, buf + wdst, wave, koff);
+        else
+          pp_copy_full<D>(src.k + (int64_t)(j + 3) * C::TILE, buf + wdst, koff);
+      } else {
         pp_copy<D, PAGED>(src.k, src, (j + 3) * BN, pb.kv_len, buf, wave, lane, koff);
+      }
     }
     if (j + 2 < n) {
       const uint32_t buf = lds0 + (uint32_t)((kBufs + (B + 2) % kBufs) * C::TILE);
-      if (!PAGED && j + 2 < n_full)
-        pp_copy_full<D>(src.v + (int64_t)(j + 2) * C::TILE, buf + wdst, voff);
-      else
+      if (j + 2 < n_full) {
+        if constexpr (PAGED)
+          pp_copy_paged<D>(src.v, src.block_bytes, ev, (j + 2) * BN, buf + wdst, wave, voff);
+        else
+          pp_copy_full<D>(src.v + (int64_t)(j + 2) * C::TILE, buf + wdst, voff);
+      } else {
         pp_copy<D, PAGED>(src.v, src, (j + 2) * BN, pb.kv_len, buf, wave, lane, voff);
+      }
+    }
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int s = 0; s < C::CP; ++s) {
+        ev[s] = ek[s];
+        ek[s] = table_row(j + 4, s);
+      }
     }
     if (j < wt) {
       const int n0 = j * BN;
@@ -840,19 +652,26 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_kernel(PrefillArgs a,
   run_pp<D, false, CAUSAL>(pb, src, c, lds);
 }
 
-// Paged prefill: sequences with q_len >= 2 of a paged batch (chunked prefill).
-// Their K/V tiles are gathered through the block table; q/o are token-major.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void paged_prefill_bf16_kernel(PagedArgs a, float c,
-                                                                          int n_qt) {
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg<D, NW>::LDS];
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  int unit, qt;
-  logical_to_work(logical, a.num_seqs * a.Hq, n_qt, unit, qt);
-  const int n = unit / a.Hq, h = unit % a.Hq;
-  const int t0 = a.qsl[n];
-  const int q_len = a.qsl[n + 1] - t0;
-  if (q_len < 2 || qt * Cfg<D, NW>::BM >= q_len) return;  // uniform over the workgroup
+// Chunked prefill of a paged batch: the sequences with q_len >= 2 (their
+// K/V tiles gathered through the block table), with the two-group kernel.
+// Work items are (sequence, 256-row query tile, query head).
+//
+// PERSISTENT (batches of up to kPagedMaxSeqs sequences): the items are
+// listed sequence by sequence over the chunk sequences only. Each workgroup
+// first reads query_start_loc once and stages, per sequence, the index of
+// its first item and its first query row in LDS; it then takes items
+// logical, logical + gridDim.x, ... until the list ends. A batch that mixes
+// a few chunks with many single-token decodes thus launches no workgroup
+// without work. Consecutive items (the query heads of one tile, GQA siblings
+// first) go to workgroups on one XCD, whose L2 then serves their shared K/V
+// tiles.
+// Otherwise one workgroup per (query tile, sequence, head) of the host's
+// bound; workgroups of sequences with fewer rows exit at once.
+constexpr int kPagedMaxSeqs = 2048;
+
+template <int D>
+__device__ __forceinline__ void run_paged_item(const PagedArgs& a, float c, char* lds, int n,
+                                               int qt, int h, int t0, int q_len) {
   const int L = a.seq_lens[n];
   const int g = h / (a.Hq / a.Hkv);
   Problem pb;
@@ -864,16 +683,79 @@ __global__ __launch_bounds__(NW * 64, 2) void paged_prefill_bf16_kernel(PagedArg
   pb.q_len = q_len;
   pb.kv_len = L;
   pb.ctx = L - q_len;
-  pb.m0 = qt * Cfg<D, NW>::BM;
+  pb.m0 = qt * kPPBM;
   KvSrc<true> src;
   src.k = (const char*)((const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D);
   src.v = (const char*)((const uint16_t*)a.v_cache + (int64_t)g * kBlockSize * D);
   src.table = a.block_table + (int64_t)n * a.max_blocks_per_seq;
   src.block_bytes = (int64_t)a.Hkv * kBlockSize * D * 2;
-  run_tile<D, NW, true, true>(pb, src, c, lds);
+  run_pp<D, true, true>(pb, src, c, lds);
 }
 
-constexpr int kNW = 4;
+template <int D, bool PERSISTENT>
+__global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_paged_kernel(PagedArgs a, float c,
+                                                                         int n_qt) {
+  __shared__ __attribute__((aligned(1024))) char lds[PP<D>::LDS];
+  if constexpr (!PERSISTENT) {
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    int unit, qt;
+    logical_to_work(logical, a.num_seqs * a.Hq, n_qt, unit, qt);
+    const int n = unit / a.Hq, h = unit % a.Hq;
+    const int t0 = a.qsl[n];
+    const int q_len = a.qsl[n + 1] - t0;
+    if (q_len < 2 || qt * kPPBM >= q_len) return;  // uniform over the workgroup
+    run_paged_item<D>(a, c, lds, n, qt, h, t0, q_len);
+  } else {
+    __shared__ int first_item[kPagedMaxSeqs];  // query tiles before sequence n
+    __shared__ int first_row[kPagedMaxSeqs];   // qsl[n]
+    __shared__ int n_items;
+    if (threadIdx.x < 64) {
+      // wave 0: per-sequence query-tile counts (0 for q_len < 2) and their
+      // exclusive prefix sums, 64 sequences at a time
+      const int lane = threadIdx.x;
+      int base = 0;
+      for (int n0 = 0; n0 < a.num_seqs; n0 += 64) {
+        const int n = n0 + lane;
+        int t0 = 0, cnt = 0;
+        if (n < a.num_seqs) {
+          t0 = a.qsl[n];
+          const int q_len = a.qsl[n + 1] - t0;
+          cnt = q_len >= 2 ? (q_len + kPPBM - 1) / kPPBM : 0;
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int dd = 1; dd < 64; dd <<= 1) {
+          const int up = __shfl_up(incl, dd);
+          incl += lane >= dd ? up : 0;
+        }
+        if (n < a.num_seqs) {
+          first_item[n] = base + incl - cnt;
+          first_row[n] = t0;
+        }
+        base += __shfl(incl, 63);
+      }
+      if (lane == 0) n_items = base;
+    }
+    __syncthreads();
+    const int items = n_items * a.Hq;
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    for (int item = logical; item < items; item += gridDim.x) {
+      const int idx = item / a.Hq, h = item % a.Hq;
+      // the sequence holding query tile idx: the largest n with
+      // first_item[n] <= idx (sequences without tiles share the next one's
+      // first item and come before it)
+      int lo = 0, hi = a.num_seqs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first_item[mid] <= idx) lo = mid; else hi = mid - 1;
+      }
+      const int n = __builtin_amdgcn_readfirstlane(lo);
+      const int t0 = first_row[n];
+      run_paged_item<D>(a, c, lds, n, idx - first_item[n], h, t0, a.qsl[n + 1] - t0);
+      __syncthreads();  // the next item refills the LDS buffers
+    }
+  }
+}
 
 }  // namespace
 
@@ -898,14 +780,22 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s) {
   const float c = a.scale * kLog2e;
-  constexpr int BM = Cfg<128, kNW>::BM;
-  const int n_qt = (a.max_query_len + BM - 1) / BM;
-  const dim3 grid((unsigned)(n_qt * a.num_seqs * a.Hq));
-  const dim3 block(kNW * 64);
-  if (a.d == 128)
-    hipLaunchKernelGGL((paged_prefill_bf16_kernel<128, kNW>), grid, block, 0, s, a, c, n_qt);
-  else
-    hipLaunchKernelGGL((paged_prefill_bf16_kernel<64, kNW>), grid, block, 0, s, a, c, n_qt);
+  const int n_qt = (a.max_query_len + kPPBM - 1) / kPPBM;
+  const int64_t bound = (int64_t)n_qt * a.num_seqs * a.Hq;  // items, at most
+  const dim3 block(kPPW * 64);
+  if (a.num_seqs <= kPagedMaxSeqs) {
+    const dim3 grid((unsigned)std::min<int64_t>(bound, device_cu_count()));
+    if (a.d == 128)
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<128, true>), grid, block, 0, s, a, c, n_qt);
+    else
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<64, true>), grid, block, 0, s, a, c, n_qt);
+  } else {
+    const dim3 grid((unsigned)bound);
+    if (a.d == 128)
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<128, false>), grid, block, 0, s, a, c, n_qt);
+    else
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<64, false>), grid, block, 0, s, a, c, n_qt);
+  }
   return hipGetLastError();
 }
 

@@ -147,17 +147,27 @@ def permute_blocks(batch, seed):
 
 
 def mixed_batch_inputs(n_chunks=8, chunk_len=512, n_decode=256, decode_len_range=(1024, 32768),
-                       Hq=32, Hkv=8, d=128, seed=5, device="cpu", poison=False):
+                       Hq=32, Hkv=8, d=128, seed=5, device="cpu", poison=False,
+                       chunk_len_range=None):
     """Mixed paged batch: ``n_chunks`` prefill chunks of ``chunk_len`` new
-    tokens (no prior context, their K/V already in the pool) followed by
-    ``n_decode`` single-token decodes whose lengths are uniform integers in
-    ``decode_len_range`` (drawn on the CPU from ``seed``). One shuffled pool
+    tokens followed by ``n_decode`` single-token decodes whose lengths are
+    uniform integers in ``decode_len_range`` (drawn on the CPU from ``seed``).
+    The chunks have no prior context (their sequences are ``chunk_len``
+    long), unless ``chunk_len_range`` is given: then each chunk's sequence
+    length is a uniform integer in that range (drawn after the decode
+    lengths), so the chunk follows L - chunk_len cached tokens. The K/V of
+    every token, new ones included, is already in the pool. One shuffled pool
     holds every sequence; on ``device="cuda"`` the values are drawn there.
     """
     g = torch.Generator().manual_seed(int(seed))
     lo, hi = decode_len_range
     dec_lens = torch.randint(lo, hi + 1, (n_decode,), generator=g).tolist()
-    seq_lens = [chunk_len] * n_chunks + dec_lens
+    if chunk_len_range is None:
+        chunk_lens = [chunk_len] * n_chunks
+    else:
+        clo, chi = chunk_len_range
+        chunk_lens = torch.randint(max(clo, chunk_len), chi + 1, (n_chunks,), generator=g).tolist()
+    seq_lens = chunk_lens + dec_lens
     q_lens = [chunk_len] * n_chunks + [1] * n_decode
     return paged_inputs(n_chunks + n_decode, Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens,
                         seed=seed, device=device, poison=poison)
