@@ -657,17 +657,19 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_kernel(PrefillArgs a,
 // Work items are (sequence, 256-row query tile, query head).
 //
 // PERSISTENT (batches of up to kPagedMaxSeqs sequences): the items are
-// listed sequence by sequence over the chunk sequences only. Each workgroup
-// first reads query_start_loc once and stages, per sequence, the index of
-// its first item and its first query row in LDS; it then takes items
-// logical, logical + gridDim.x, ... until the list ends. A batch that mixes
-// a few chunks with many single-token decodes thus launches no workgroup
-// without work. Consecutive items (the query heads of one tile, GQA siblings
-// first) go to workgroups on one XCD, whose L2 then serves their shared K/V
-// tiles.
+// listed over the chunk sequences only, longest sequence first and, within
+// a sequence, its last query tile (the most keys) first. Each workgroup
+// builds that list once in LDS (the chunk sequences, their order and the
+// index of each one's first item), then takes one item per round, the
+// rounds alternating direction over the workgroups, until the list ends: a
+// static longest-first assignment. A batch that mixes a few chunks with many
+// single-token decodes thus launches no workgroup without work. Consecutive
+// items (the query heads of one tile, GQA siblings first) go to workgroups
+// on one XCD, whose L2 then serves their shared K/V tiles.
 // Otherwise one workgroup per (query tile, sequence, head) of the host's
 // bound; workgroups of sequences with fewer rows exit at once.
 constexpr int kPagedMaxSeqs = 2048;
+constexpr int kSortMax = 128;  // chunk sequences ordered by length, at most
 
 template <int D>
 __device__ __forceinline__ void run_paged_item(const PagedArgs& a, float c, char* lds, int n,
@@ -706,21 +708,51 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_paged_kernel(PagedArg
     if (q_len < 2 || qt * kPPBM >= q_len) return;  // uniform over the workgroup
     run_paged_item<D>(a, c, lds, n, qt, h, t0, q_len);
   } else {
-    __shared__ int first_item[kPagedMaxSeqs];  // query tiles before sequence n
-    __shared__ int first_row[kPagedMaxSeqs];   // qsl[n]
-    __shared__ int n_items;
+    // the chunk sequences, longest first (up to kSortMax of them; more keep
+    // batch order), with the index of each one's first item
+    __shared__ int seq_of[kPagedMaxSeqs];      // r-th chunk sequence
+    __shared__ int first_of[kPagedMaxSeqs];    // its first query tile in the list
+    __shared__ int scratch[kPagedMaxSeqs];
+    __shared__ int n_chunk_seqs, n_tiles;
     if (threadIdx.x < 64) {
-      // wave 0: per-sequence query-tile counts (0 for q_len < 2) and their
-      // exclusive prefix sums, 64 sequences at a time
+      // wave 0. Pass 1: compact the sequences with q_len >= 2, in batch order,
+      // into scratch (ids) and first_of (lengths)
       const int lane = threadIdx.x;
-      int base = 0;
+      int m = 0;
       for (int n0 = 0; n0 < a.num_seqs; n0 += 64) {
         const int n = n0 + lane;
-        int t0 = 0, cnt = 0;
-        if (n < a.num_seqs) {
-          t0 = a.qsl[n];
-          const int q_len = a.qsl[n + 1] - t0;
-          cnt = q_len >= 2 ? (q_len + kPPBM - 1) / kPPBM : 0;
+        const bool chunk = n < a.num_seqs && a.qsl[n + 1] - a.qsl[n] >= 2;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(chunk);
+        if (chunk) {
+          const int at = m + (int)__builtin_popcountll(bal & ((1ull << lane) - 1));
+          scratch[at] = n;
+          first_of[at] = a.seq_lens[n];
+        }
+        m += (int)__builtin_popcountll(bal);
+      }
+      // Pass 2: order by length, longest first (rank by counting; ties keep
+      // batch order), into seq_of
+      if (m <= kSortMax) {
+        for (int i = lane; i < m; i += 64) {
+          const int Li = first_of[i];
+          int rank = 0;
+          for (int j = 0; j < m; ++j) {
+            const int Lj = first_of[j];
+            rank += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
+          }
+          seq_of[rank] = scratch[i];
+        }
+      } else {
+        for (int i = lane; i < m; i += 64) seq_of[i] = scratch[i];
+      }
+      // Pass 3: first item of each, in that order
+      int base = 0;
+      for (int r0 = 0; r0 < m; r0 += 64) {
+        const int r = r0 + lane;
+        int cnt = 0;
+        if (r < m) {
+          const int n = seq_of[r];
+          cnt = (a.qsl[n + 1] - a.qsl[n] + kPPBM - 1) / kPPBM;
         }
         int incl = cnt;
 #pragma unroll
@@ -728,30 +760,39 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_paged_kernel(PagedArg
           const int up = __shfl_up(incl, dd);
           incl += lane >= dd ? up : 0;
         }
-        if (n < a.num_seqs) {
-          first_item[n] = base + incl - cnt;
-          first_row[n] = t0;
-        }
+        if (r < m) first_of[r] = base + incl - cnt;
         base += __shfl(incl, 63);
       }
-      if (lane == 0) n_items = base;
+      if (lane == 0) {
+        n_chunk_seqs = m;
+        n_tiles = base;
+      }
     }
     __syncthreads();
-    const int items = n_items * a.Hq;
-    const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    for (int item = logical; item < items; item += gridDim.x) {
+    const int m = n_chunk_seqs;
+    const int items = n_tiles * a.Hq;
+    const int G = gridDim.x;
+    const int logical = xcd_logical(blockIdx.x, G);
+    // rounds alternate direction (0 .. G-1, then G-1 .. 0), so the workgroup
+    // that took the longest item of one round takes the shortest of the next
+    for (int k = 0;; ++k) {
+      const int item = k * G + ((k & 1) ? G - 1 - logical : logical);
+      if (item >= items) break;
       const int idx = item / a.Hq, h = item % a.Hq;
-      // the sequence holding query tile idx: the largest n with
-      // first_item[n] <= idx (sequences without tiles share the next one's
-      // first item and come before it)
-      int lo = 0, hi = a.num_seqs - 1;
+      // the chunk sequence holding query tile idx: the largest r with
+      // first_of[r] <= idx
+      int lo = 0, hi = m - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (first_item[mid] <= idx) lo = mid; else hi = mid - 1;
+        if (first_of[mid] <= idx) lo = mid; else hi = mid - 1;
       }
-      const int n = __builtin_amdgcn_readfirstlane(lo);
-      const int t0 = first_row[n];
-      run_paged_item<D>(a, c, lds, n, idx - first_item[n], h, t0, a.qsl[n + 1] - t0);
+      const int r = __builtin_amdgcn_readfirstlane(lo);
+      const int n = seq_of[r];
+      const int t0 = a.qsl[n];
+      const int q_len = a.qsl[n + 1] - t0;
+      const int cnt = (q_len + kPPBM - 1) / kPPBM;
+      // within a sequence, its last query tile (the most keys) first
+      run_paged_item<D>(a, c, lds, n, cnt - 1 - (idx - first_of[r]), h, t0, q_len);
       __syncthreads();  // the next item refills the LDS buffers
     }
   }
