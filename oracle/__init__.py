@@ -1,5 +1,5 @@
-"""CPU fp64 oracle for fused causal attention, paged decode and the paged
-cache append.
+"""CPU fp64 oracle for fused causal attention, paged decode, the paged cache
+append and the residual-add + RMSNorm fusion.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this package:
 only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
@@ -27,4 +27,5 @@ from .attention import (  # noqa: F401
     decode_paged,
     gather_paged_kv,
     kv_append,
+    add_rmsnorm,
 )

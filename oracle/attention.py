@@ -223,3 +223,24 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, query_start
             kc[blk, :, t % block_size, :] = kn[t0 + i]
             vc[blk, :, t % block_size, :] = vn[t0 + i]
     return kc, vc
+
+
+def add_rmsnorm(x, residual, weight, eps):
+    """Residual addition followed by RMS normalisation, row by row, in fp64.
+
+    The pages name "a residual connection added, then an RMSNorm" as a common
+    fusion ("Fast attention kernels and operator fusion", section "Operator
+    fusion", second paragraph) without writing it out; this is the usual
+    definition, over the last axis (``hidden``):
+
+        h = x + residual
+        y = h / sqrt(mean(h * h) + eps) * weight
+
+    x, residual: [..., hidden]; weight: [hidden]. Returns (y, h) in float64
+    (h is the new residual stream).
+    """
+    h = _as_f64(x) + _as_f64(residual)
+    w = _as_f64(weight)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    y = h / np.sqrt(ms + float(eps)) * w
+    return y, h

@@ -416,3 +416,46 @@ def test_kv_append_keeps_bf16_bits():
     assert list(kc[1, 0, 2]) == list(k_new.view(torch.int16).numpy()[0, 0])
     assert list(vc[1, 0, 2]) == list(v_new.view(torch.int16).numpy()[0, 0])
     assert not np.any(kc[0]) and not np.any(kc[1, 0, :2])
+
+
+# ---- residual add + RMSNorm ---------------------------------------------
+
+def test_add_rmsnorm_hand_worked_golden():
+    # tests/golden/add_rmsnorm_hand.json: every value worked out by hand
+    cases = json.load(open(os.path.join(HERE, "golden", "add_rmsnorm_hand.json")))["cases"]
+    for c in cases:
+        y, h = oracle.add_rmsnorm(np.array(c["x"]), np.array(c["residual"]), np.array(c["weight"]),
+                                  c["eps"])
+        np.testing.assert_allclose(h, np.array(c["h"]), rtol=0, atol=1e-15, err_msg=c["name"])
+        np.testing.assert_allclose(y, np.array(c["y"]), rtol=1e-14, atol=1e-15, err_msg=c["name"])
+
+
+def test_add_rmsnorm_unit_rms_and_scale_invariance():
+    # with eps = 0 and unit weight every output row has mean square exactly 1,
+    # and scaling both inputs by alpha leaves y unchanged
+    x = RNG.standard_normal((5, 37))
+    r = RNG.standard_normal((5, 37))
+    y, h = oracle.add_rmsnorm(x, r, np.ones(37), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+    y2, _ = oracle.add_rmsnorm(3.5 * x, 3.5 * r, np.ones(37), 0.0)
+    np.testing.assert_allclose(y2, y, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(h, x + r)
+
+
+def test_add_rmsnorm_weight_multiplies_columns():
+    x = RNG.standard_normal((3, 16))
+    r = RNG.standard_normal((3, 16))
+    w = RNG.standard_normal(16)
+    y1, _ = oracle.add_rmsnorm(x, r, np.ones(16), 1e-5)
+    yw, _ = oracle.add_rmsnorm(x, r, w, 1e-5)
+    np.testing.assert_allclose(yw, y1 * w, rtol=1e-14, atol=1e-15)
+
+
+def test_add_rmsnorm_matches_torch_rms_norm_fp64():
+    # library special case: torch.nn.functional.rms_norm on the sum, in fp64
+    x = torch.randn(4, 64, dtype=torch.float64)
+    r = torch.randn(4, 64, dtype=torch.float64)
+    w = torch.randn(64, dtype=torch.float64)
+    y, _ = oracle.add_rmsnorm(x, r, w, 1e-6)
+    ref = torch.nn.functional.rms_norm(x + r, (64,), weight=w, eps=1e-6)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)

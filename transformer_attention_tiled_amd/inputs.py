@@ -182,6 +182,17 @@ def new_kv_rows(num_tokens, Hkv, d, seed, dtype=torch.bfloat16, device="cpu"):
     return k, v
 
 
+def norm_inputs(rows, hidden, seed, dtype=torch.bfloat16, device="cpu"):
+    """Inputs of the residual-add + RMSNorm fusion: x and residual [rows, hidden]
+    i.i.d. N(0,1), weight [hidden] = 1 + 0.1 N(0,1), each rounded to ``dtype``
+    (draw order x, residual, weight)."""
+    g = _gen(seed, device)
+    x = torch.randn(rows, hidden, generator=g, device=device, dtype=torch.float32).to(dtype)
+    r = torch.randn(rows, hidden, generator=g, device=device, dtype=torch.float32).to(dtype)
+    w = (1.0 + 0.1 * torch.randn(hidden, generator=g, device=device, dtype=torch.float32)).to(dtype)
+    return x, r, w
+
+
 def compact_sequences(batch, seqs):
     """CPU copy of just the physical blocks that the given sequences use.
 
