@@ -370,6 +370,42 @@ def single(args, dev):
         return {"workload": w, "ms": round(ms, 5), "rows": nt, "bytes": by,
                 "gbs": round(by / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if w in ("addnorm", "addnorm_decode"):
+        # residual add + RMSNorm, bf16, hidden 4096 (32 heads x 128): 4096 rows
+        # (a prefill chunk) or 256 rows (a decode batch); 4 rotated buffer sets
+        # (~0.5 GB for 4096 rows, beyond the last-level cache). The calls are
+        # replayed from a HIP graph, so the events see GPU time.
+        rows, hidden = (4096, 4096) if w == "addnorm" else (256, 4096)
+        sets = []
+        for i in range(4):
+            x, r, wt = inputs.norm_inputs(rows, hidden, 140 + i, device=dev)
+            sets.append((x, r, wt, torch.empty_like(x), torch.empty_like(x)))
+
+        def call(j):
+            x, r, wt, y, h = sets[j]
+            attn.add_rmsnorm(x, r, wt, 1e-6, out=y, residual_out=h)
+        for j in range(4):
+            call(j)
+        torch.cuda.synchronize()
+        per_graph = 16
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(per_graph):
+                call(c % 4)
+        for _ in range(max(1, args.warmup // 4)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(max(1, args.steps // 4)):
+            e = t.start()
+            graph.replay()
+            t.stop(e)
+        torch.cuda.synchronize()
+        ms = t.mean_ms() / per_graph
+        by = 4 * rows * hidden * 2 + hidden * 2  # x, residual read; out, residual_out written
+        return {"workload": w, "ms": round(ms, 5), "rows": rows, "hidden": hidden, "bytes": by,
+                "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     if w == "decode_step":
         # one serving decode step on the 64-sequence batch (Hq=12, Hkv=2,
         # d=128, lengths uniform in [256, 4096]): append the 64 new K/V rows
@@ -441,7 +477,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "c1", "c2", "c3", "c4", "c5", "c5ctx", "append",
-                             "append_decode", "decode_step", "copy"])
+                             "append_decode", "decode_step", "addnorm", "addnorm_decode",
+                             "copy"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition length for decode (0: the library's choice)")
     args = ap.parse_args()

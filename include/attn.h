@@ -2,8 +2,9 @@
  * attn.h — C ABI of libattn.so: fused scaled-dot-product attention on AMD
  * Instinct MI355X (gfx950).
  *
- * Two operations, as the source pages state the problem, and the cache
- * append that feeds the second (attn_kv_append, below):
+ * Two operations, as the source pages state the problem, the cache append
+ * that feeds the second (attn_kv_append) and the residual-add + RMSNorm
+ * fusion the same page names (attn_add_rmsnorm), both below:
  *
  *  - attn_prefill: causal (or full) attention over contiguous Q, K, V,
  *    computed block by block so that the T x T score matrix never reaches
@@ -191,6 +192,27 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
                    const int32_t* query_start_loc, int num_seqs, int num_tokens, int Hkv, int d,
                    int block_size, int max_blocks_per_seq, int max_query_len, int64_t num_blocks,
                    attn_dtype dtype, void* stream);
+
+/*
+ * attn_add_rmsnorm — residual addition fused with RMS normalisation, the
+ * fusion the pages name next to attention: unfused, the sum is written to
+ * HBM and read back by the norm ("Fast attention kernels and operator
+ * fusion", the-ai.news, section "Operator fusion", second paragraph). Per
+ * row of `hidden` elements:
+ *   residual_out = x + residual
+ *   out          = (x + residual) / sqrt(mean((x + residual)^2) + eps) * weight
+ * computed in fp32 from the bf16 inputs; both results rounded to bf16 (RNE).
+ *
+ * Layout (row-major, bf16): x, residual, out, residual_out: [rows][hidden];
+ * weight: [hidden]. residual_out may be residual itself (the residual stream
+ * updated in place); no other pair may overlap.
+ * Supported: dtype ATTN_BF16; hidden a multiple of 8 and at most 16384;
+ * eps finite and >= 0; all pointers 16-byte aligned.
+ * Returns ATTN_OK or a negative status; on error nothing is launched.
+ */
+int attn_add_rmsnorm(const void* x, const void* residual, const void* weight, void* out,
+                     void* residual_out, int rows, int hidden, float eps, attn_dtype dtype,
+                     void* stream);
 
 /* attn_status_string — static, human-readable text for a status code. */
 const char* attn_status_string(int status);

@@ -148,3 +148,23 @@ def append(lib, kn=P, vn=P2, kc=P3, vc=P4, table=P4 + 0x40000000, seq_lens=P4 + 
 ])
 def test_kv_append_rejects(lib, kw, code):
     assert append(lib, **kw) == code
+
+
+def add_rmsnorm(lib, x=P, r=P2, w=P3, out=P4, rout=P4 + 0x10000000, rows=4, hidden=4096,
+                eps=1e-6, dtype=BF16):
+    return lib.attn_add_rmsnorm(x, r, w, out, rout, rows, hidden, ctypes.c_float(eps), dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(r=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL),
+    (dict(rout=None), NULL),
+    (dict(dtype=F32), UNSUP), (dict(hidden=16384 + 8), UNSUP), (dict(eps=-1.0), UNSUP),
+    (dict(eps=float("nan")), UNSUP),
+    (dict(rows=0), SHAPE), (dict(hidden=0), SHAPE), (dict(hidden=100), SHAPE),
+    (dict(x=P + 8), ALIGN), (dict(w=P3 + 4), ALIGN), (dict(rout=P4 + 0x10000002), ALIGN),
+    (dict(out=P), SHAPE),                  # output overlaps x
+    (dict(rout=P), SHAPE),                 # residual output overlaps x
+    (dict(rout=P2 + 0x100), SHAPE),        # partial overlap with residual (only exact in place is allowed)
+])
+def test_add_rmsnorm_rejects(lib, kw, code):
+    assert add_rmsnorm(lib, **kw) == code

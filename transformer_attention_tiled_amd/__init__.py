@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     decode_paged_workspace_size,
     decode_paged_partition_size,
     kv_append,
+    add_rmsnorm,
     status_string,
     library_path,
     load_library,

@@ -76,6 +76,9 @@ def load_library():
                                    c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                    ctypes.c_int64, c_int, c_void_p]
     lib.attn_kv_append.restype = c_int
+    lib.attn_add_rmsnorm.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                     c_int, c_float, c_int, c_void_p]
+    lib.attn_add_rmsnorm.restype = c_int
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -190,3 +193,24 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, *, max_quer
         block_table.shape[1], int(max_query_len), num_blocks, _dtype_code(k_new.dtype),
         _stream(k_new.device))
     _check(status, "attn_kv_append")
+
+
+def add_rmsnorm(x, residual, weight, eps, *, out=None, residual_out=None):
+    """attn_add_rmsnorm on [rows, hidden] tensors: returns (out, residual_out),
+    out = RMSNorm(x + residual) * weight and residual_out = x + residual.
+    Pass residual_out=residual to update the residual stream in place."""
+    lib = load_library()
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    for name, t in (("x", x), ("residual", residual), ("weight", weight)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    status = lib.attn_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(weight), _ptr(out),
+                                  _ptr(residual_out), rows, hidden, float(eps),
+                                  _dtype_code(x.dtype), _stream(x.device))
+    _check(status, "attn_add_rmsnorm")
+    return out, residual_out

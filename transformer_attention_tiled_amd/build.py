@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
-           "kv_append.hip"]
+           "kv_append.hip", "add_rmsnorm.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -1,0 +1,118 @@
+// Residual addition fused with RMS normalisation, bf16 in and out, fp32
+// arithmetic, for gfx950.
+//
+// The pages name "a residual connection added, then an RMSNorm" as a common
+// fusion: unfused, the sum is written to HBM and read back by the norm
+// ("Fast attention kernels and operator fusion", the-ai.news, section
+// "Operator fusion", second paragraph). Per row of `hidden` elements:
+//   h = x + residual                              (written: the new residual)
+//   y = h / sqrt(mean(h^2) + eps) * weight        (written)
+// Each element of x and residual is read once and each of y and h written
+// once; the sum never leaves registers between the two steps, so the kernel
+// moves 8 bytes per element and is bound by HBM bandwidth.
+//
+// Work decomposition: one workgroup of 256 threads per row. Thread t owns
+// the 16-byte chunks t, t + 256, ... of the row (CH of them at most), so
+// every load and store is a whole 16-byte vector and the 256 threads cover
+// consecutive 4 KiB spans. The row's sum of squares is reduced within each
+// wave by lane exchanges, then across the 4 waves through LDS.
+#include <hip/hip_runtime.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+  const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+  return a | (b << 16);
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(NormArgs a) {
+  __shared__ float wave_sums[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int nch = a.hidden / 8;  // 16-byte chunks per row
+  const int64_t row = (int64_t)blockIdx.x * a.hidden;
+  const u32x4* x = (const u32x4*)((const uint16_t*)a.x + row);
+  const u32x4* r = (const u32x4*)((const uint16_t*)a.residual + row);
+  u32x4* h_out = (u32x4*)((uint16_t*)a.residual_out + row);
+  u32x4* y_out = (u32x4*)((uint16_t*)a.out + row);
+  const u32x4* w = (const u32x4*)a.weight;
+
+  // loads first (all in flight together), then the sums
+  u32x4 xv[CH], rv[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = i * kThreads + tid;
+    if (c < nch) {
+      xv[i] = x[c];
+      rv[i] = r[c];
+    }
+  }
+  float h[CH][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = i * kThreads + tid;
+    if (c < nch) {
+      u32x4 hv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[i][2 * q] = bf16_lo(xv[i][q]) + bf16_lo(rv[i][q]);
+        h[i][2 * q + 1] = bf16_hi(xv[i][q]) + bf16_hi(rv[i][q]);
+        ss = __builtin_fmaf(h[i][2 * q], h[i][2 * q], ss);
+        ss = __builtin_fmaf(h[i][2 * q + 1], h[i][2 * q + 1], ss);
+        hv[q] = pack_bf16(h[i][2 * q], h[i][2 * q + 1]);
+      }
+      h_out[c] = hv;  // the same thread read this chunk of residual above
+    }
+  }
+  // row sum of squares: lanes, then waves
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  if ((tid & 63) == 0) wave_sums[tid >> 6] = ss;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) total += wave_sums[i];
+  const float inv = rsqrtf(total / (float)a.hidden + a.eps);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = i * kThreads + tid;
+    if (c < nch) {
+      const u32x4 wv = w[c];
+      u32x4 yv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        yv[q] = pack_bf16(h[i][2 * q] * inv * bf16_lo(wv[q]),
+                          h[i][2 * q + 1] * inv * bf16_hi(wv[q]));
+      y_out[c] = yv;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_add_rmsnorm_bf16(const NormArgs& a, hipStream_t s) {
+  const int chunks = (a.hidden / 8 + kThreads - 1) / kThreads;  // per thread
+  const dim3 grid((unsigned)a.rows), block(kThreads);
+  if (chunks <= 1)
+    hipLaunchKernelGGL((add_rmsnorm_kernel<1>), grid, block, 0, s, a);
+  else if (chunks <= 2)
+    hipLaunchKernelGGL((add_rmsnorm_kernel<2>), grid, block, 0, s, a);
+  else if (chunks <= 4)
+    hipLaunchKernelGGL((add_rmsnorm_kernel<4>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((add_rmsnorm_kernel<8>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -234,4 +234,34 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
   return ATTN_OK;
 }
 
+int attn_add_rmsnorm(const void* x, const void* residual, const void* weight, void* out,
+                     void* residual_out, int rows, int hidden, float eps, attn_dtype dtype,
+                     void* stream) {
+  if (x == nullptr || residual == nullptr || weight == nullptr || out == nullptr ||
+      residual_out == nullptr)
+    return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (rows < 1 || hidden < 8 || hidden % 8 != 0) return ATTN_ERR_SHAPE;
+  if (hidden > attn::kNormMaxHidden) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
+      !aligned(residual_out, 16))
+    return ATTN_ERR_ALIGN;
+  const int64_t bytes = (int64_t)rows * hidden * 2;
+  const int64_t wbytes = (int64_t)hidden * 2;
+  // residual_out may be residual itself (in-place update), nothing else may overlap
+  if (overlap(out, bytes, x, bytes) || overlap(out, bytes, residual, bytes) ||
+      overlap(out, bytes, weight, wbytes) || overlap(out, bytes, residual_out, bytes) ||
+      overlap(residual_out, bytes, x, bytes) || overlap(residual_out, bytes, weight, wbytes) ||
+      (residual_out != residual && overlap(residual_out, bytes, residual, bytes)))
+    return ATTN_ERR_SHAPE;
+  if (rows > kMaxGrid) return ATTN_ERR_SHAPE;
+  attn::NormArgs a;
+  a.x = x; a.residual = residual; a.weight = weight; a.out = out; a.residual_out = residual_out;
+  a.rows = rows; a.hidden = hidden; a.eps = eps;
+  if (attn::launch_add_rmsnorm_bf16(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_LAUNCH;
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -54,6 +54,18 @@ struct AppendArgs {
   int max_blocks_per_seq, max_query_len;
 };
 
+// Residual add + RMSNorm over rows of `hidden` elements.
+struct NormArgs {
+  const void* x;         // [rows][hidden]
+  const void* residual;  // [rows][hidden]
+  const void* weight;    // [hidden]
+  void* out;             // [rows][hidden]: RMSNorm(x + residual) * weight
+  void* residual_out;    // [rows][hidden]: x + residual (may be `residual` itself)
+  int rows, hidden;
+  float eps;
+};
+constexpr int kNormMaxHidden = 8 * 256 * 8;  // 8 chunks of 16 bytes per thread
+
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;  // tokens per split-KV partition, at most
 
@@ -69,5 +81,6 @@ hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s);  // q_l
 hipError_t launch_paged_decode_bf16(const PagedArgs& a, hipStream_t s);   // q_len == 1 sequences
 int append_grid(int num_tokens);  // workgroups of the append launch
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t s);
+hipError_t launch_add_rmsnorm_bf16(const NormArgs& a, hipStream_t s);
 
 }  // namespace attn
