@@ -1,5 +1,5 @@
-"""A decode step (cache append, then paged attention) captured in a HIP graph
-and replayed: the pages' remedy for launch-bound steps is to record the GPU
+"""A decode step (cache append, then paged attention), and a prefill,
+captured in a HIP graph and replayed: the pages' remedy for launch-bound steps is to record the GPU
 work once and resubmit it whole, which needs fixed shapes and fixed addresses
 ("Fast attention kernels and operator fusion", the-ai.news, section "Fusion
 and CUDA Graphs with torch.compile"). Every replay, with eager work and
@@ -104,3 +104,41 @@ def test_captured_decode_step_replays_match_eager_and_oracle():
                                      1.0 / math.sqrt(d))
         assert_close(o_g, ro, torch.bfloat16, f"graph replay {rep}")
         assert_lse_close(lse_g, rl, f"graph replay {rep}")
+
+
+def test_captured_prefill_replays_match_eager():
+    # attn_prefill captured once (fixed shapes and addresses), replayed three
+    # times with new q/k/v contents copied into the captured tensors and eager
+    # work in between; every replay equals the eager call bit for bit
+    print("[graph] prefill, 3 replays", flush=True)
+    B, Hq, Hkv, T, d = 2, 8, 2, 700, 128
+    q0, k0, v0 = inputs.prefill_inputs(B, Hq, Hkv, T, d, seed=400)
+    q, k, v = q0.to(DEV), k0.to(DEV), v0.to(DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, T, device=DEV)
+    attn.prefill(q, k, v, o, causal=True, lse=lse)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn.prefill(q, k, v, o, causal=True, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        qn, kn, vn = inputs.prefill_inputs(B, Hq, Hkv, T, d, seed=401 + rep)
+        q.copy_(qn.to(DEV))
+        k.copy_(kn.to(DEV))
+        v.copy_(vn.to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_g, lse_g = o.clone(), lse.clone()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        o.zero_()
+        attn.prefill(q, k, v, o, causal=True, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o), f"replay {rep}: o differs from the eager call"
+        assert torch.equal(lse_g, lse), f"replay {rep}: lse differs from the eager call"
+        del junk
+        if rep == 0:  # and once against the oracle, on two heads
+            ro, rl = oracle.prefill(qn, kn, vn, 1.0 / math.sqrt(d), causal=True, heads=[0, 5])
+            assert_close(o_g[:, [0, 5]], ro[:, [0, 5]], torch.bfloat16, "graph prefill")
+            assert_lse_close(lse_g[:, [0, 5]], rl[:, [0, 5]], "graph prefill lse")
