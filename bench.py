@@ -241,7 +241,7 @@ def headline(args, dev):
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": measured_traffic(
-                                "decode_kernel<128> 64 seqs Hq=12 Hkv=2 (mean of 4 rotated pools)")},
+                                "decode_kernel<128> 64 seqs Hq=12 Hkv=2 (mean of 8 rotated pools)")},
         "cpu_baseline": {"value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads(),
                          "kind": "oracle",
                          "sample": f"fp64 numpy oracle on the even query heads of the prefill "
