@@ -578,26 +578,46 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   }
   if (grp == 0) phase_barrier();
 
-  // epilogue: o = O / l, lse = m*ln2 + ln(l)
+  // epilogue: o = O / l, lse = m*ln2 + ln(l).
+  // The accumulators give each lane 4 consecutive d of one query row, so a
+  // direct store instruction would write 16-byte pieces of 32 rows. Instead
+  // the wave stages its 32 x D tile in LDS (free now: the last barrier came
+  // after every wave's last LDS read and copy) and writes whole rows, 64 x 16
+  // bytes per instruction, with a streaming (non-temporal) hint: the output
+  // then does not sit dirty in the last-level cache, to be written back while
+  // the next kernel on the stream reads HBM.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int qrow = wq0 + lq;
-  if (qrow < pb.q_len) {
-    uint16_t* orow = pb.o + (int64_t)qrow * pb.row_stride;
+  {
+    // row-major tile, 16-byte chunks XOR-swizzled by row so that the 32 rows
+    // of one staging write spread over the banks
+    lds_char* wtile = (lds_char*)(uintptr_t)(lds0 + (uint32_t)(wave * 32 * C::ROW));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hf;
         const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 0] * inv));
         const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 1] * inv));
         const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 2] * inv));
         const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * g4 + 3] * inv));
-        *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+        const int ch = 4 * db + g4;  // d = 8 ch + 4 hf .. +3
+        lds_char* p = wtile + lq * C::ROW + ((ch ^ (lq & (C::NCH - 1))) * 16) + 8 * hf;
+        *(u32x2 __attribute__((address_space(3)))*)p = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
       }
-    if (pb.lse != nullptr && hf == 0)
-      pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 32 * C::NCH / 64; ++s) {
+      const int idx = 64 * s + lane;
+      const int r = idx / C::NCH, ch = idx % C::NCH;
+      const u32x4 val = *(const u32x4 __attribute__((address_space(3)))*)(
+          wtile + r * C::ROW + ((ch ^ (r & (C::NCH - 1))) * 16));
+      if (wq0 + r < pb.q_len)
+        __builtin_nontemporal_store(val, (u32x4*)(pb.o + (int64_t)(wq0 + r) * pb.row_stride + 8 * ch));
+    }
   }
+  const int qrow = wq0 + lq;
+  if (qrow < pb.q_len && pb.lse != nullptr && hf == 0)
+    pb.lse[(int64_t)qrow * pb.lse_stride] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : kNegInf;
 }
 
 // Workgroup id -> logical work index. Consecutive workgroup ids are spread
