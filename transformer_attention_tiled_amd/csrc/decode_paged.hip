@@ -86,6 +86,10 @@ struct Tile {
 
 // One 16-byte-per-lane HBM -> LDS copy: lane L's bytes at `src` go to LDS
 // address lds + 16 L.
+// M0 holds the LDS address and is set inside the same asm statement; it is
+// declared clobbered, and the compiler keeps no value of its own in M0 across
+// these statements (on gfx950 LDS instructions do not read M0), so its
+// warning that a reserved register is clobbered is expected here.
 __device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds), "v"(src) : "memory", "m0");

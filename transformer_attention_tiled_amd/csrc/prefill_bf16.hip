@@ -97,6 +97,10 @@ __device__ __forceinline__ int sigma32(int i) {
 
 // HBM -> LDS copy, 16 bytes per lane to LDS address lds + 16 L.
 // Scalar 64-bit base + per-lane 32-bit byte offset.
+// M0 holds the LDS address and is set inside the same asm statement; it is
+// declared clobbered, and the compiler keeps no value of its own in M0 across
+// these statements (on gfx950 LDS instructions do not read M0), so its
+// warning that a reserved register is clobbered is expected here.
 __device__ __forceinline__ void copy_saddr(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
