@@ -272,7 +272,8 @@ def single(args, dev):
         peak = PEAK_F32_TFLOPS if cfg[5] == torch.float32 else PEAK_BF16_TFLOPS
         tf = fl / (ms * 1e-3) / 1e12
         return {"workload": w, "ms": round(ms, 5), "tflops": round(tf, 3),
-                "frac_peak": round(tf / peak, 4), "dtype": str(cfg[5]).replace("torch.", "")}
+                "frac_peak": round(tf / peak, 4), "flops": fl,
+                "dtype": str(cfg[5]).replace("torch.", "")}
     if w == "c4":
         dsets = make_decode_sets(ROTATE, 64, 12, 2, 128, 256, 4096, 4, dev)
         for i in range(args.warmup):
@@ -289,7 +290,8 @@ def single(args, dev):
         by = sum(decode_bytes(bd, 12, 2, 128) for bd in used) / len(used)
         gbs = by / (ms * 1e-3) / 1e9
         return {"workload": w, "ms": round(ms, 5), "gbs": round(gbs, 1),
-                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "partition_size": PARTITION or
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(by),
+                "partition_size": PARTITION or
                 attn.decode_paged_partition_size(64, 2, max(bd["max_seq_len"] for bd in dsets))}
     if w in ("c5", "c5ctx"):
         # 8 chunks of 512 new tokens + 256 decodes, lengths uniform in
