@@ -464,12 +464,14 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   auto step = [&](const int j, auto bconst) {
     constexpr int B = decltype(bconst)::value;
     // ---- M(j): O^T += V^T P^T (tile j-1), then S^T = K Q^T (tile j).
-    // Always both products, so the phase is one block: before the first
-    // tile P is 0 and the V buffer read is zero-filled; after the wave's
-    // last tile P is 0; a product of K with a buffer that holds no tile of
-    // this workgroup yet is computed and ignored.
-    m_phase<D, true, true, B * C::TILE, ((B + kBufs - 1) % kBufs) * C::TILE>(acc, sc, pk, qf,
-                                                                             vaddr, kaddr);
+    // Both products, so the phase is one block: before the first tile P is
+    // 0 and the V buffer read is zero-filled; at the wave's last tile wt the
+    // scores are computed and ignored. A wave past its last tile (j > wt:
+    // P of tile j-1 is 0 and the scores unused) skips the phase and only
+    // keeps to the barriers.
+    if (j <= wt)
+      m_phase<D, true, true, B * C::TILE, ((B + kBufs - 1) % kBufs) * C::TILE>(acc, sc, pk, qf,
+                                                                               vaddr, kaddr);
     // this wave's copies of K tile j+1 and V tile j (issued at the start of
     // S(j-2)) have landed; the barrier after the later group's M(j) makes
     // every wave's copies visible before either group's M(j+1). Only the
