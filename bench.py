@@ -322,8 +322,10 @@ def single(args, dev):
         # chunk flops: row i of a chunk after c cached tokens sees c + i + 1 keys
         fl = sum(4.0 * 32 * 128 * (512 * (L - 512) + 512 * 513 / 2) for L in chunk_lens)
         kv = (sum(dec_lens) + sum(chunk_lens)) * 8 * 128 * 2 * 2
+        dec_kv = sum(dec_lens) * 8 * 128 * 2 * 2
         return {"workload": w, "ms": round(ms, 4), "partition_size": PARTITION,
-                "chunk_gflop": round(fl / 1e9, 2),
+                "chunk_gflop": round(fl / 1e9, 2), "chunk_flops": fl,
+                "decode_kv_bytes": dec_kv, "chunk_kv_bytes": kv - dec_kv,
                 "kv_gbytes": round(kv / 1e9, 3), "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1)}
     if w in ("append", "append_decode"):
         # paged-cache append: "append" writes the mixed batch's new rows (8
