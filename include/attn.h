@@ -145,6 +145,10 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
  * that sees no key (L_n = 0) gets o = 0 and lse = -inf.
  * Supported: d in {64, 128}; dtype ATTN_BF16; block_size == 16;
  * Hq % Hkv == 0 and Hq / Hkv <= 16.
+ * What the call writes (o, lse, the first
+ * attn_decode_paged_workspace_size(...) bytes of workspace) must not overlap
+ * any input (q, the caches, block_table, seq_lens, query_start_loc) or
+ * another output: ATTN_ERR_SHAPE.
  * Returns ATTN_OK or a negative status; on error nothing is launched.
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -183,8 +187,9 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * map to the same cache slot (otherwise which one lands is unspecified).
  * Supported: d in {64, 128}; dtype ATTN_BF16; block_size == 16. Pointers of
  * k_new, v_new and the caches 16-byte aligned; the new rows must not overlap
- * the caches. max_query_len >= every q_len_n (1 when query_start_loc is
- * NULL).
+ * the caches, the two caches must not overlap each other, block_table,
+ * seq_lens or query_start_loc (ATTN_ERR_SHAPE). max_query_len >= every
+ * q_len_n (1 when query_start_loc is NULL).
  * Returns ATTN_OK or a negative status; on error nothing is launched.
  */
 int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

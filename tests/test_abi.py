@@ -93,7 +93,14 @@ def decode(lib, q=P, kc=P2, vc=P3, table=P4, seq_lens=P4 + 0x10000, qsl=None, o=
     (dict(max_query_len=200, qsl=P4 + 0x30000, num_tokens=300), SHAPE),
     (dict(q=P + 4), ALIGN), (dict(table=P4 + 2), ALIGN), (dict(ws=0x4000000 + 16), ALIGN),
     (dict(ws=None), WS), (dict(ws_bytes=16), WS),
-    (dict(o=P), SHAPE),
+    (dict(o=P), SHAPE),                                  # o overlaps q
+    (dict(o=P4), SHAPE),                                 # o overlaps the block table
+    (dict(lse=P4 + 0x10000), SHAPE),                     # lse overlaps seq_lens
+    (dict(lse=P4 + 0x20000), SHAPE),                     # lse overlaps o
+    (dict(ws=P2), SHAPE),                                # workspace overlaps the K cache
+    (dict(ws=P4 + 0x10000), SHAPE),                      # workspace overlaps seq_lens
+    (dict(ws=P4 + 0x20000), SHAPE),                      # workspace overlaps o
+    (dict(qsl=P4 + 0x20000, max_query_len=2), SHAPE),    # o overlaps query_start_loc
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
@@ -145,6 +152,9 @@ def append(lib, kn=P, vn=P2, kc=P3, vc=P4, table=P4 + 0x40000000, seq_lens=P4 + 
     (dict(kn=P + 8), ALIGN), (dict(kc=P3 + 4), ALIGN), (dict(table=P4 + 0x40000002), ALIGN),
     (dict(kn=P3), SHAPE),                       # new rows overlap the K cache
     (dict(vc=P3 + 0x1000), SHAPE),              # the two caches overlap
+    (dict(table=P3 + 0x1000), SHAPE),           # the block table lies inside the K cache
+    (dict(seq_lens=P4 + 0x100), SHAPE),         # seq_lens lies inside the V cache
+    (dict(qsl=P3 + 0x2000), SHAPE),             # query_start_loc lies inside the K cache
 ])
 def test_kv_append_rejects(lib, kw, code):
     assert append(lib, **kw) == code

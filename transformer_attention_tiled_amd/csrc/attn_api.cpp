@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -66,17 +67,18 @@ namespace attn {
 
 int device_cu_count() {
   constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};  // 0: not queried yet (same value if two threads race)
+  // 0: not queried yet; threads that race both store the same value
+  static std::atomic<int> cached[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cached[dev] == 0) {
-    int cu = 0;
+  int cu = cached[dev].load(std::memory_order_relaxed);
+  if (cu == 0) {
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cu <= 0)
       cu = 256;
-    cached[dev] = cu;
+    cached[dev].store(cu, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cu;
 }
 
 }  // namespace attn
@@ -167,14 +169,28 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4) ||
       !aligned(lse, 4) || !aligned(workspace, 256))
     return ATTN_ERR_ALIGN;
-  const int64_t qbytes = (int64_t)num_tokens * Hq * d * 2;
-  const int64_t cbytes = num_blocks * Hkv * attn::kBlockSize * d * 2;
-  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_cache, cbytes) ||
-      overlap(o, qbytes, v_cache, cbytes) || overlap(lse, (int64_t)num_tokens * Hq * 4, o, qbytes))
-    return ATTN_ERR_SHAPE;
   WsLayout w;
   if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
+  {
+    // what the call writes (o, lse, the workspace) overlaps nothing it reads
+    // and no other output
+    const void* in[] = {q, k_cache, v_cache, block_table, seq_lens, query_start_loc};
+    const int64_t in_bytes[] = {(int64_t)num_tokens * Hq * d * 2,
+                                num_blocks * Hkv * attn::kBlockSize * d * 2,
+                                num_blocks * Hkv * attn::kBlockSize * d * 2,
+                                (int64_t)num_seqs * max_blocks_per_seq * 4,
+                                (int64_t)num_seqs * 4, (int64_t)(num_seqs + 1) * 4};
+    const void* out[] = {o, lse, workspace};
+    const int64_t out_bytes[] = {(int64_t)num_tokens * Hq * d * 2, (int64_t)num_tokens * Hq * 4,
+                                 (int64_t)w.total};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 6; ++j)
+        if (overlap(out[i], out_bytes[i], in[j], in_bytes[j])) return ATTN_ERR_SHAPE;
+      for (int j = i + 1; j < 3; ++j)
+        if (overlap(out[i], out_bytes[i], out[j], out_bytes[j])) return ATTN_ERR_SHAPE;
+    }
+  }
   if ((int64_t)w.max_parts * Hkv * num_seqs > kMaxGrid) return ATTN_ERR_SHAPE;
   const int64_t n_qt = ((int64_t)max_query_len + 255) / 256;  // 256-row query tiles
   if (n_qt * num_seqs * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
@@ -218,10 +234,17 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
     return ATTN_ERR_ALIGN;
   const int64_t nbytes = (int64_t)num_tokens * Hkv * d * 2;
   const int64_t cbytes = num_blocks * Hkv * attn::kBlockSize * d * 2;
+  const int64_t tbytes = (int64_t)num_seqs * max_blocks_per_seq * 4;
+  const int64_t sbytes = (int64_t)num_seqs * 4, qslbytes = (int64_t)(num_seqs + 1) * 4;
   if (overlap(k_cache, cbytes, v_cache, cbytes) || overlap(k_new, nbytes, k_cache, cbytes) ||
       overlap(k_new, nbytes, v_cache, cbytes) || overlap(v_new, nbytes, k_cache, cbytes) ||
       overlap(v_new, nbytes, v_cache, cbytes))
     return ATTN_ERR_SHAPE;
+  // the caches (written) overlap none of the metadata the call reads
+  for (const void* c : {(const void*)k_cache, (const void*)v_cache})
+    if (overlap(c, cbytes, block_table, tbytes) || overlap(c, cbytes, seq_lens, sbytes) ||
+        overlap(c, cbytes, query_start_loc, qslbytes))
+      return ATTN_ERR_SHAPE;
   if ((int64_t)attn::append_grid(num_tokens) > kMaxGrid) return ATTN_ERR_SHAPE;
 
   attn::AppendArgs a;
