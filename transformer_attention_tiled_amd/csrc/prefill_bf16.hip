@@ -529,43 +529,55 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
             sc[kb][r] = dead ? kNegInf : sc[kb][r];
           }
       }
-      // max over this lane's 32 keys; the row max (both lane halves) is only
-      // needed when some lane's reference max must move
-      float mx = kNegInf;
+      // weights p = 2^(s*c - m) against the current reference max m: rounded
+      // to bf16 for the product with V, summed in fp32 (v_dot2 on the packed
+      // weights would be fewer instructions, but it cannot issue while the
+      // other wave's MFMAs occupy the matrix core; plain adds can)
+      auto weights = [&]() -> float {
+        const float mu = (m_run == kNegInf) ? 0.f : m_run;
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleThreshold)) {
-        const float mt = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-        const bool need = mt > m_run + kRescaleThreshold;
-        const float m_new = need ? mt : m_run;
-        const float alpha =
-            (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int e = 0; e < 8; ++e) {
+              const float pv =
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, -mu));
+              pk[2 * kb + h][e] = (__bf16)pv;
+              part[e & 3] += pv;
+            }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      float ts = weights();
+      // The reference max must move when the tile's max exceeds it by more
+      // than 8 (log2 units), i.e. when some weight exceeds 2^8; then this
+      // lane's sum exceeds 2^8 too. Only then (or while a lane has no
+      // reference yet) is the tile max computed, the same decision taken
+      // as when it is computed up front, and the weights recomputed, so the
+      // result is the same; most tiles skip the max entirely.
+      if (__builtin_amdgcn_ballot_w64(ts > 256.f || m_run == kNegInf)) {
+        float mx = kNegInf;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleThreshold)) {
+          const float mt = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+          const bool need = mt > m_run + kRescaleThreshold;
+          const float m_new = need ? mt : m_run;
+          const float alpha =
+              (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+          ts = weights();
+        }
       }
-      // weights p = 2^(s*c - m): rounded to bf16 for the product with V,
-      // summed in fp32 (v_dot2 on the packed weights would be fewer
-      // instructions, but it cannot issue while the other wave's MFMAs
-      // occupy the matrix core; plain adds can)
-      const float mu = (m_run == kNegInf) ? 0.f : m_run;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, -mu));
-            pk[2 * kb + h][e] = (__bf16)pv;
-            part[e & 3] += pv;
-          }
-      l_run += (part[0] + part[1]) + (part[2] + part[3]);
+      l_run += ts;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
