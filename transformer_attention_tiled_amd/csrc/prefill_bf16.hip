@@ -428,6 +428,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
   float m_run = kNegInf;  // reference max, log2 units
+  float nmu = 0.f;        // -m_run, or 0 while there is no reference
   float l_run = 0.f;      // partial row sum over this lane's keys
   const int qpos = pb.ctx + wq0 + lq;
   // Paged: the table entries of this wave's copy rows, read with scalar loads
@@ -534,8 +535,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
       // weights would be fewer instructions, but it cannot issue while the
       // other wave's MFMAs occupy the matrix core; plain adds can)
       auto weights = [&]() -> float {
-        const float mu = (m_run == kNegInf) ? 0.f : m_run;
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -543,9 +543,14 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float pv =
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, -mu));
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, nmu));
               pk[2 * kb + h][e] = (__bf16)pv;
-              part[e & 3] += pv;
+              // each partial sum starts with its first weight (weights are
+              // never -0, so this is the sum from 0)
+              if (kb == 0 && h == 0 && e < 4)
+                part[e & 3] = pv;
+              else
+                part[e & 3] += pv;
             }
         return (part[0] + part[1]) + (part[2] + part[3]);
       };
@@ -569,6 +574,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
           const float alpha =
               (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
+          nmu = (m_run == kNegInf) ? 0.f : -m_run;
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
