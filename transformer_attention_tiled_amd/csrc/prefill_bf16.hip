@@ -521,13 +521,18 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
       const int n0 = j * BN;
       const bool diag = CAUSAL ? (n0 + BN - 1 > pb.ctx + wq0) : false;
       if (diag || n0 + BN > pb.kv_len) {
+        // register (kb, r) holds key n0 + 8 hf + o, o = 32 kb + 16 (r >> 3) +
+        // (r & 7) a constant; the key is dead when past this lane's query
+        // (o > qpos - n0 - 8 hf) or past the keys (o >= kv_len - n0 - 8 hf):
+        // one bound per lane, one compare per register
+        const int tk = pb.kv_len - n0 - 8 * hf;
+        const int t = CAUSAL ? min(qpos - n0 - 8 * hf + 1, tk) : tk;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);
-            const bool dead = (CAUSAL && key > qpos) || key >= pb.kv_len;
-            sc[kb][r] = dead ? kNegInf : sc[kb][r];
+            const int o = 32 * kb + 16 * (r >> 3) + (r & 7);
+            sc[kb][r] = o >= t ? kNegInf : sc[kb][r];
           }
       }
       // weights p = 2^(s*c - m) against the current reference max m: rounded
