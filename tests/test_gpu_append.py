@@ -12,7 +12,7 @@ import torch
 import oracle
 import transformer_attention_tiled_amd as attn
 from transformer_attention_tiled_amd import inputs
-from parity import assert_close, assert_lse_close
+from parity import assert_close, assert_lse_close, ref_decode
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -101,7 +101,7 @@ def test_append_then_decode_step():
                               b["seq_lens"])
     rk = torch.from_numpy(rk).view(torch.bfloat16)
     rv = torch.from_numpy(rv).view(torch.bfloat16)
-    ro, rl = oracle.decode_paged(b["q"], rk, rv, b["block_table"], b["seq_lens"],
+    ro, rl = ref_decode(b["q"], rk, rv, b["block_table"], b["seq_lens"],
                                  1.0 / math.sqrt(128))
     assert_close(o, ro, torch.bfloat16, "append + decode")
     assert_lse_close(lse, rl, "append + decode")

@@ -9,7 +9,7 @@ import torch
 import oracle
 import transformer_attention_tiled_amd as attn
 from transformer_attention_tiled_amd import inputs
-from parity import assert_close, assert_lse_close
+from parity import assert_close, assert_lse_close, ref_decode
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -31,8 +31,8 @@ def run(b, partition_size=0, with_qsl=False, want_lse=True):
 
 
 def reference(b):
-    return oracle.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
-                               b["seq_lens"], 1.0 / math.sqrt(b["q"].shape[-1]))
+    return ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+                      b["seq_lens"], 1.0 / math.sqrt(b["q"].shape[-1]))
 
 
 def check(b, partition_size=0, with_qsl=False, what=""):

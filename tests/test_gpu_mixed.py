@@ -11,7 +11,7 @@ import torch
 import oracle
 import transformer_attention_tiled_amd as attn
 from transformer_attention_tiled_amd import inputs
-from parity import assert_close, assert_lse_close
+from parity import assert_close, assert_lse_close, ref_decode, ref_prefill
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -37,7 +37,7 @@ def test_small_mixed_with_context(seed):
     print(f"[mixed] small seed={seed}", flush=True)
     b = inputs.paged_inputs(len(seq_lens), 8, 2, 128, seq_lens=seq_lens, q_lens=q_lens, seed=seed)
     o, lse = run(b)
-    ro, rl = oracle.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
                                  b["seq_lens"], 1.0 / math.sqrt(128),
                                  query_start_loc=b["query_start_loc"])
     assert_close(o, ro, torch.bfloat16, "mixed")
@@ -49,7 +49,7 @@ def test_mixed_d64_gqa4():
     q_lens = [128, 1, 200]
     b = inputs.paged_inputs(3, 16, 4, 64, seq_lens=seq_lens, q_lens=q_lens, seed=72)
     o, lse = run(b)
-    ro, rl = oracle.decode_paged(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
                                  b["seq_lens"], 1.0 / math.sqrt(64),
                                  query_start_loc=b["query_start_loc"])
     assert_close(o, ro, torch.bfloat16, "mixed d64")
@@ -91,7 +91,7 @@ def test_mixed_many_sequences_direct_grid():
     dec = sorted(set(int(x) for x in rng.choice(2100, 40, replace=False)) - set(chunks))
     seqs = chunks + dec
     kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
-    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, 1.0 / math.sqrt(64), query_start_loc=qsl_c)
+    ro, rl = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(64), query_start_loc=qsl_c)
     qsl = b["query_start_loc"]
     rows = torch.cat([torch.arange(int(qsl[n]), int(qsl[n + 1])) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "2100 sequences")
@@ -118,7 +118,7 @@ def test_config_mixed_batch_full_size_sampled():
     pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
     seqs = list(range(8)) + sorted(pick)
     kc, vc, table, sl, q, qsl = inputs.compact_sequences(b, seqs)
-    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl)
+    ro, rl = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl)
     qsl_full = b["query_start_loc"].cpu()
     rows = torch.cat([torch.arange(int(qsl_full[n]), int(qsl_full[n + 1])) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "full-size mixed")
@@ -157,7 +157,7 @@ def test_config_mixed_batch_with_context_full_size_sampled():
         V = oracle.gather_paged_kv(vc, table[0].numpy(), L).transpose(1, 0, 2)[None]
         Q = np.zeros((1, 32, L, 128))
         Q[0, :, ctx:] = q.double().numpy().transpose(1, 0, 2)
-        ro, rl = oracle.prefill(Q, K, V, scale, causal=True, rows=[ctx + i for i in picks])
+        ro, rl = ref_prefill(Q, K, V, scale, causal=True, rows=[ctx + i for i in picks])
         rows = torch.tensor([int(qsl[n]) + i for i in picks])
         got = o[rows.to(DEV)].transpose(0, 1)  # [Hq, rows, d]
         assert_close(got, ro[0], torch.bfloat16, f"chunk {n} (context {ctx})")
@@ -167,7 +167,7 @@ def test_config_mixed_batch_with_context_full_size_sampled():
     pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
     seqs = sorted(pick)
     kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
-    ro, rl = oracle.decode_paged(q, kc, vc, table, sl, scale, query_start_loc=qsl_c)
+    ro, rl = ref_decode(q, kc, vc, table, sl, scale, query_start_loc=qsl_c)
     rows = torch.tensor([int(qsl[n]) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "decodes next to context chunks")
     assert_lse_close(lse[rows.to(DEV)], rl, "decodes next to context chunks")

@@ -239,6 +239,12 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
   // Q and the table entries have landed before any copy is issued: from here
   // on, the only outstanding loads are the ring copies, counted exactly.
   __builtin_amdgcn_s_waitcnt(0);
+  // fold the softmax scale in log2 units (c = scale * log2 e) into q: the
+  // score MFMA then yields c * s (each q * c rounded to bf16, as in prefill)
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c);
 
   const int64_t bstride = (int64_t)a.Hkv * kBlockSize * D;
   const uint16_t* kbase = (const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D;
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * c;
+    const float mt = mx;
     const bool need = mt > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(need)) {
       // per-head decision: heads that do not need it keep m and scale by 1
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
     float ps[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ps[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mu));
+      ps[r] = __builtin_amdgcn_exp2f(s[r] - mu);
       pa[r] = (__bf16)ps[r];
     }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);

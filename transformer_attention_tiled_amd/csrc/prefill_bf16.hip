@@ -58,6 +58,11 @@
 // rescaled by 2^(m_old - m_new) only when the tile's max exceeds m by more
 // than 8 (then p <= 2^8 at most, harmless in fp32 and bf16). The final
 // o = O / l is exact whatever reference m was used.
+// The softmax phase's vector work competes with the other wave's MFMAs, so
+// it is kept to exp2, bf16 rounding and sums: Q is multiplied by
+// c = scale * log2(e) once (rounded to bf16) and the score MFMA starts from
+// -m instead of 0, so it yields t - m itself; the tile max is computed only
+// when some lane's weights sum past 2^8 (a weight past 2^8 implies it).
 //
 // Causal tile skipping: a workgroup visits only the key tiles up to its last
 // query; a wave skips the compute of tiles entirely after its own 32 rows.
@@ -272,7 +277,7 @@ __device__ __forceinline__ void pp_copy_paged(const char* base, int64_t block_by
 template <int D, bool DO_PV, bool DO_S, int KOFF, int VOFF>
 __device__ __forceinline__ void m_phase(f32x16* acc, f32x16* sc, const bf16x8* pk,
                                         const bf16x8* qf, const uint32_t* vabs,
-                                        const uint32_t* kabs) {
+                                        const uint32_t* kabs, const f32x16& cinit) {
   using C = PP<D>;
   constexpr int LOOKAHEAD = 8;
   constexpr int NPV = DO_PV ? 4 * (D / 32) : 0;  // MFMAs, 2 transpose reads each
@@ -298,8 +303,8 @@ __device__ __forceinline__ void m_phase(f32x16* acc, f32x16* sc, const bf16x8* p
     }
   }
   if constexpr (DO_S) {
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
+    sc[0] = cinit;
+    sc[1] = cinit;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
@@ -408,6 +413,12 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   pp_copy<D, PAGED>(src.v, src, 0, pb.kv_len, vbuf(0), wave, lane, voff);
   if (2 < n) pp_copy<D, PAGED>(src.k, src, 2 * BN, pb.kv_len, kbuf(2), wave, lane, koff);
   if (1 < n) pp_copy<D, PAGED>(src.v, src, BN, pb.kv_len, vbuf(1), wave, lane, voff);
+  // fold the softmax scale in log2 units (c = scale * log2 e) into Q, once:
+  // the score MFMA then yields c * s directly (each q * c rounded to bf16)
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c);
   {
     // M(0) multiplies P = 0 with the V buffer of "tile -1": make it zeros
     // (V tile 3, the first copy into that buffer, is issued in S(1), after
@@ -429,6 +440,9 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
   float m_run = kNegInf;  // reference max, log2 units
   float nmu = 0.f;        // -m_run, or 0 while there is no reference
+  // the score MFMA starts from nmu instead of 0, so it yields c * s - m_run:
+  // the exponent of the weight, with no further vector work
+  f32x16 negm = f32x16{};
   float l_run = 0.f;      // partial row sum over this lane's keys
   const int qpos = pb.ctx + wq0 + lq;
   // Paged: the table entries of this wave's copy rows, read with scalar loads
@@ -472,7 +486,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
     // keeps to the barriers.
     if (j <= wt)
       m_phase<D, true, true, B * C::TILE, ((B + kBufs - 1) % kBufs) * C::TILE>(acc, sc, pk, qf,
-                                                                               vaddr, kaddr);
+                                                                               vaddr, kaddr, negm);
     // this wave's copies of K tile j+1 and V tile j (issued at the start of
     // S(j-2)) have landed; the barrier after the later group's M(j) makes
     // every wave's copies visible before either group's M(j+1). Only the
@@ -547,8 +561,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float pv =
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * h + e], c, nmu));
+              const float pv = __builtin_amdgcn_exp2f(sc[kb][8 * h + e]);
               pk[2 * kb + h][e] = (__bf16)pv;
               // each partial sum starts with its first weight (weights are
               // never -0, so this is the sum from 0)
@@ -572,19 +585,29 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleThreshold)) {
-          const float mt = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        const float tmax = mx - nmu;  // this lane's max of c * s
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleThreshold)) {
+          const float mt = fmaxf(tmax, __shfl_xor(tmax, 32));
           const bool need = mt > m_run + kRescaleThreshold;
           const float m_new = need ? mt : m_run;
           const float alpha =
               (!need || m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
-          nmu = (m_run == kNegInf) ? 0.f : -m_run;
+          const float nmu_new = (m_run == kNegInf) ? 0.f : -m_run;
+          const float dm = nmu_new - nmu;
+          nmu = nmu_new;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) negm[r] = nmu;
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+          // this tile's scores against the new reference
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[kb][r] += dm;
           ts = weights();
         }
       }
