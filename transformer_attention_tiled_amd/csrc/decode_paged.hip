@@ -239,12 +239,6 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
   // Q and the table entries have landed before any copy is issued: from here
   // on, the only outstanding loads are the ring copies, counted exactly.
   __builtin_amdgcn_s_waitcnt(0);
-  // fold the softmax scale in log2 units (c = scale * log2 e) into q: the
-  // score MFMA then yields c * s (each q * c rounded to bf16, as in prefill)
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c);
 
   const int64_t bstride = (int64_t)a.Hkv * kBlockSize * D;
   const uint16_t* kbase = (const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D;
@@ -270,6 +264,13 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u)
     if (u < nb) issue(u);
+  // fold the softmax scale in log2 units (c = scale * log2 e) into q while
+  // the first blocks are in flight: the score MFMA then yields c * s (each
+  // q * c rounded to bf16, as in prefill)
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c);
 
   for (int b = 0; b < nb; ++b) {
     if (b + kRing - 1 < nb) issue(b + kRing - 1);
