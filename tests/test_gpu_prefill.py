@@ -129,6 +129,27 @@ def test_constant_v():
     assert_close(o, expect, torch.bfloat16, "constant v")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_running_max_moves_on_most_tiles(d):
+    # Keys drift toward the (positive) queries, so each row's scores climb by
+    # about 8.5 log2 units per 64-key tile, around the lazy-rescale threshold
+    # of 8: most rows move their reference max on most tiles, some rows skip
+    # some tiles. Exercises the rescale path (tile max, new reference, scores
+    # shifted and weights recomputed) far more than N(0,1) inputs do.
+    print(f"[prefill] growing scores d={d}", flush=True)
+    B, Hq, Hkv, T = 1, 4, 2, 1024
+    g = torch.Generator().manual_seed(31 + d)
+    q = (torch.randn(B, Hq, T, d, generator=g).abs() + 0.5).to(torch.bfloat16)
+    a = 4.54 / math.sqrt(d)  # per-tile climb 1.4427 * a * E[q] * sqrt(d), E[q] ~ 1.3
+    ramp = (torch.arange(T, dtype=torch.float32) / 64.0)[None, None, :, None]
+    k = (0.1 * torch.randn(B, Hkv, T, d, generator=g) + a * ramp).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    o, lse = run(q, k, v, True)
+    ref_o, ref_lse = ref_prefill(q, k, v, 1.0 / math.sqrt(d), causal=True)
+    assert_close(o, ref_o, torch.bfloat16, f"growing scores d={d}")
+    assert_lse_close(lse, ref_lse, f"growing scores d={d}")
+
+
 def test_rejects_unsupported_without_fallback():
     q, k, v = inputs.prefill_inputs(1, 2, 2, 16, 96, torch.bfloat16, seed=25)
     with pytest.raises(attn.AttnError) as e:
