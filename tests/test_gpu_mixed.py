@@ -44,6 +44,33 @@ def test_small_mixed_with_context(seed):
     assert_lse_close(lse, rl, "mixed")
 
 
+def test_growing_scores_paged_chunks_and_decodes():
+    # Positive queries and keys that drift toward them with their position
+    # (about 8.5 log2 units per 64 positions): the running max moves on most
+    # tiles of the chunk kernel and most blocks of the split-KV decode, in
+    # rows that see context and rows that do not.
+    seq_lens = [900, 1500, 257, 2000]
+    q_lens = [200, 1, 64, 1]
+    d, Hq, Hkv = 128, 8, 2
+    print("[mixed] growing scores", flush=True)
+    b = inputs.paged_inputs(len(seq_lens), Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens,
+                            seed=77, poison=False)
+    g = torch.Generator().manual_seed(78)
+    b["q"] = (torch.randn(b["q"].shape, generator=g).abs() + 0.5).to(torch.bfloat16)
+    a = 4.54 / math.sqrt(d)
+    kc = b["k_cache"].to(torch.float32)
+    for n, L in enumerate(seq_lens):
+        for p in range(L):
+            blk = int(b["block_table"][n, p // 16])
+            kc[blk, :, p % 16, :] = 0.1 * kc[blk, :, p % 16, :] + a * (p / 64.0)
+    b["k_cache"] = kc.to(torch.bfloat16)
+    o, lse = run(b)
+    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                        1.0 / math.sqrt(d), query_start_loc=b["query_start_loc"])
+    assert_close(o, ro, torch.bfloat16, "growing scores, paged")
+    assert_lse_close(lse, rl, "growing scores, paged")
+
+
 def test_mixed_d64_gqa4():
     seq_lens = [128, 40, 513]
     q_lens = [128, 1, 200]
