@@ -443,6 +443,9 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   // the score MFMA starts from nmu instead of 0, so it yields c * s - m_run:
   // the exponent of the weight, with no further vector work
   f32x16 negm = f32x16{};
+  // wave-uniform: every lane has a reference (m_run moves only in the
+  // rescale path below, so this is updated there)
+  bool all_ref = false;
   float l_run = 0.f;      // partial row sum over this lane's keys
   const int qpos = pb.ctx + wq0 + lq;
   // Paged: the table entries of this wave's copy rows, read with scalar loads
@@ -579,7 +582,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
       // reference yet) is the tile max computed, the same decision taken
       // as when it is computed up front, and the weights recomputed, so the
       // result is the same; most tiles skip the max entirely.
-      if (__builtin_amdgcn_ballot_w64(ts > 256.f || m_run == kNegInf)) {
+      if (__builtin_amdgcn_ballot_w64(ts > 256.f) || !all_ref) {
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -609,6 +612,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[kb][r] += dm;
           ts = weights();
+          all_ref = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
         }
       }
       l_run += ts;
