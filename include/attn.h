@@ -37,6 +37,8 @@
  *    library never falls back to another algorithm (the pages warn that a
  *    silent fallback to an unfused path is the hardest risk to see,
  *    "Hugging Face attention profiling guide", last paragraph).
+ *  - Sizes whose byte counts or grids do not fit in int64 (or in the launch
+ *    limits) return ATTN_ERR_SHAPE.
  *  - A launch failure reported by the HIP runtime returns ATTN_ERR_LAUNCH.
  *  - bf16 is IEEE bfloat16 (the upper 16 bits of an fp32). Products are
  *    accumulated in fp32. The bf16 paths fold the softmax scale into the

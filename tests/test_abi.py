@@ -66,6 +66,7 @@ def prefill(lib, q=P, k=P2, v=P3, o=P4, B=1, Hq=2, Hkv=2, T=16, d=64, scale=0.12
     (dict(q=P + 8), ALIGN), (dict(o=P4 + 4), ALIGN), (dict(lse=P + 2), ALIGN),
     (dict(o=P), SHAPE),            # output overlaps q
     (dict(lse=P4 + 64), SHAPE),    # lse overlaps o
+    (dict(B=2**20, Hq=2**20, Hkv=2**20, T=2**20), SHAPE),  # byte counts overflow int64
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
@@ -101,6 +102,11 @@ def decode(lib, q=P, kc=P2, vc=P3, table=P4, seq_lens=P4 + 0x10000, qsl=None, o=
     (dict(ws=P4 + 0x10000), SHAPE),                      # workspace overlaps seq_lens
     (dict(ws=P4 + 0x20000), SHAPE),                      # workspace overlaps o
     (dict(qsl=P4 + 0x20000, max_query_len=2), SHAPE),    # o overlaps query_start_loc
+    (dict(num_blocks=2**60), SHAPE),                     # cache bytes overflow int64
+    (dict(num_seqs=2**31 - 1, num_tokens=2**31 - 1, mbps=2**31 - 1, ws_bytes=2**60),
+     SHAPE),                                             # block-table bytes overflow int64
+    (dict(num_seqs=2**31 - 1, num_tokens=2**31 - 1, Hq=2**30, Hkv=2**30,
+          max_seq_len=2**31 - 16, mbps=2**27, ws_bytes=2**63), SHAPE),  # policy estimate
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
@@ -111,6 +117,10 @@ def test_workspace_size_and_partition_policy():
     P_auto = attn.decode_paged_partition_size(64, 2, 4096)
     assert P_auto > 0 and P_auto % 16 == 0
     assert attn.decode_paged_partition_size(0, 2, 4096) == 0
+    # sizes whose estimate or byte counts overflow int64 are out of range
+    assert attn.decode_paged_partition_size(2**31 - 1, 2**30, 2**31 - 1) == 0
+    assert attn.decode_paged_workspace_size(2**31 - 1, 2**30, 2**30, 128, 2**31 - 1, 0) == 0
+    assert attn.decode_paged_workspace_size(2**31 - 1, 2**31 - 1, 1, 128, 2**31 - 1, 16) == 0
     ws = attn.decode_paged_workspace_size(64, 12, 2, 128, 4096, 256)
     parts = 4096 // 256
     rows = 64 * 12 * parts
@@ -155,6 +165,7 @@ def append(lib, kn=P, vn=P2, kc=P3, vc=P4, table=P4 + 0x40000000, seq_lens=P4 + 
     (dict(table=P3 + 0x1000), SHAPE),           # the block table lies inside the K cache
     (dict(seq_lens=P4 + 0x100), SHAPE),         # seq_lens lies inside the V cache
     (dict(qsl=P3 + 0x2000), SHAPE),             # query_start_loc lies inside the K cache
+    (dict(num_blocks=2**60), SHAPE),            # cache bytes overflow int64
 ])
 def test_kv_append_rejects(lib, kw, code):
     assert append(lib, **kw) == code

@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -25,10 +26,27 @@ bool supported_d(int d) { return d == 64 || d == 128; }
 
 bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
+// Product of sizes in int64, or false if it overflows (absurd arguments are
+// rejected before any size derived from them is used).
+bool mul(std::initializer_list<int64_t> f, int64_t* out) {
+  int64_t p = 1;
+  for (int64_t x : f)
+    if (x < 0 || __builtin_mul_overflow(p, x, &p)) return false;
+  *out = p;
+  return true;
+}
+
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (a == nullptr || b == nullptr) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// The partition policy estimates the work as num_seqs * Hkv * (max_seq_len /
+// 2 + 1) in int64; sizes beyond that range are rejected.
+bool policy_in_range(int num_seqs, int Hkv, int max_seq_len) {
+  int64_t est;
+  return mul({num_seqs, Hkv, (int64_t)max_seq_len / 2 + 1, 2}, &est);
 }
 
 // Bytes of the split-KV workspace: partial outputs, then partial lse.
@@ -46,12 +64,15 @@ bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partit
   if (partition_size < 0 || partition_size % attn::kBlockSize != 0 ||
       partition_size > attn::kMaxPartition)
     return false;
+  if (!policy_in_range(num_seqs, Hkv, max_seq_len)) return false;
   const int P = partition_size > 0 ? partition_size
                                    : attn::decode_partition_size(num_seqs, Hkv, max_seq_len);
   if (P <= 0) return false;
   const int64_t parts = ((int64_t)max_seq_len + P - 1) / P;
-  const int64_t rows = (int64_t)num_seqs * Hq * parts;
-  const int64_t o_bytes = (rows * d * 4 + 255) / 256 * 256;
+  int64_t rows, ob;
+  if (!mul({num_seqs, Hq, parts}, &rows) || !mul({rows, d, 4}, &ob) || ob > (INT64_MAX >> 2))
+    return false;
+  const int64_t o_bytes = (ob + 255) / 256 * 256;
   const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
   w->partition_size = P;
   w->max_parts = (int)parts;
@@ -110,16 +131,18 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
       !aligned(lse, 4))
     return ATTN_ERR_ALIGN;
   const int64_t esize = dtype == ATTN_BF16 ? 2 : 4;
-  const int64_t qbytes = (int64_t)B * Hq * T * d * esize;
-  const int64_t kvbytes = (int64_t)B * Hkv * T * d * esize;
-  const int64_t lbytes = (int64_t)B * Hq * T * 4;
+  int64_t qbytes, kvbytes, lbytes;
+  if (!mul({B, Hq, T, d, esize}, &qbytes) || !mul({B, Hkv, T, d, esize}, &kvbytes) ||
+      !mul({B, Hq, T, 4}, &lbytes))
+    return ATTN_ERR_SHAPE;
   if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kvbytes) ||
       overlap(o, qbytes, v, kvbytes) || overlap(lse, lbytes, q, qbytes) ||
       overlap(lse, lbytes, k, kvbytes) || overlap(lse, lbytes, v, kvbytes) ||
       overlap(lse, lbytes, o, qbytes))
     return ATTN_ERR_SHAPE;
   // query tiles of 64 (fp32) or 128 (bf16) rows, all in one grid dimension
-  if ((int64_t)(T + 63) / 64 * B * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
+  int64_t grid;
+  if (!mul({((int64_t)T + 63) / 64, B, Hq}, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
 
   attn::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -132,6 +155,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
 }
 
 int attn_decode_paged_partition_size(int num_seqs, int Hkv, int max_seq_len) {
+  if (!policy_in_range(num_seqs, Hkv, max_seq_len)) return 0;
   return attn::decode_partition_size(num_seqs, Hkv, max_seq_len);
 }
 
@@ -175,15 +199,15 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   {
     // what the call writes (o, lse, the workspace) overlaps nothing it reads
     // and no other output
+    int64_t qb, cb, tb, lb;
+    if (!mul({num_tokens, Hq, d, 2}, &qb) || !mul({num_blocks, Hkv, attn::kBlockSize, d, 2}, &cb) ||
+        !mul({num_seqs, max_blocks_per_seq, 4}, &tb) || !mul({num_tokens, Hq, 4}, &lb))
+      return ATTN_ERR_SHAPE;
     const void* in[] = {q, k_cache, v_cache, block_table, seq_lens, query_start_loc};
-    const int64_t in_bytes[] = {(int64_t)num_tokens * Hq * d * 2,
-                                num_blocks * Hkv * attn::kBlockSize * d * 2,
-                                num_blocks * Hkv * attn::kBlockSize * d * 2,
-                                (int64_t)num_seqs * max_blocks_per_seq * 4,
-                                (int64_t)num_seqs * 4, (int64_t)(num_seqs + 1) * 4};
+    const int64_t in_bytes[] = {qb, cb, cb, tb, (int64_t)num_seqs * 4,
+                                (int64_t)(num_seqs + 1) * 4};
     const void* out[] = {o, lse, workspace};
-    const int64_t out_bytes[] = {(int64_t)num_tokens * Hq * d * 2, (int64_t)num_tokens * Hq * 4,
-                                 (int64_t)w.total};
+    const int64_t out_bytes[] = {qb, lb, (int64_t)w.total};
     for (int i = 0; i < 3; ++i) {
       for (int j = 0; j < 6; ++j)
         if (overlap(out[i], out_bytes[i], in[j], in_bytes[j])) return ATTN_ERR_SHAPE;
@@ -191,9 +215,11 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
         if (overlap(out[i], out_bytes[i], out[j], out_bytes[j])) return ATTN_ERR_SHAPE;
     }
   }
-  if ((int64_t)w.max_parts * Hkv * num_seqs > kMaxGrid) return ATTN_ERR_SHAPE;
+  int64_t g1, g2;
   const int64_t n_qt = ((int64_t)max_query_len + 255) / 256;  // 256-row query tiles
-  if (n_qt * num_seqs * Hq > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (!mul({w.max_parts, Hkv, num_seqs}, &g1) || g1 > kMaxGrid ||
+      !mul({n_qt, num_seqs, Hq}, &g2) || g2 > kMaxGrid)
+    return ATTN_ERR_SHAPE;
 
   attn::PagedArgs a;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -232,9 +258,11 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
       !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
       !aligned(query_start_loc, 4))
     return ATTN_ERR_ALIGN;
-  const int64_t nbytes = (int64_t)num_tokens * Hkv * d * 2;
-  const int64_t cbytes = num_blocks * Hkv * attn::kBlockSize * d * 2;
-  const int64_t tbytes = (int64_t)num_seqs * max_blocks_per_seq * 4;
+  int64_t nbytes, cbytes, tbytes;
+  if (!mul({num_tokens, Hkv, d, 2}, &nbytes) ||
+      !mul({num_blocks, Hkv, attn::kBlockSize, d, 2}, &cbytes) ||
+      !mul({num_seqs, max_blocks_per_seq, 4}, &tbytes))
+    return ATTN_ERR_SHAPE;
   const int64_t sbytes = (int64_t)num_seqs * 4, qslbytes = (int64_t)(num_seqs + 1) * 4;
   if (overlap(k_cache, cbytes, v_cache, cbytes) || overlap(k_new, nbytes, k_cache, cbytes) ||
       overlap(k_new, nbytes, v_cache, cbytes) || overlap(v_new, nbytes, k_cache, cbytes) ||
