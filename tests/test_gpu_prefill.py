@@ -66,6 +66,16 @@ def test_bf16_non_causal(T, d):
     case(2, 2, 1, T, d, torch.bfloat16, False, seed=300 + T)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(2, 8, 2, 600, 128), (3, 8, 2, 515, 64),
+                                          (1, 16, 4, 777, 128)])
+def test_bf16_several_units_per_xcd(B, Hq, Hkv, T, d):
+    # (batch, head) units a multiple of 8, so each XCD owns several of them,
+    # with GQA 4 and several query tiles of 256 rows, the last one ragged:
+    # the workgroup -> (unit, query tile) mapping of the long prefill at a
+    # size the full oracle covers
+    case(B, Hq, Hkv, T, d, torch.bfloat16, True, seed=400 + T)
+
+
 def test_config_bf16_b4_t2048():
     # B=4, Hq=Hkv=16, T=2048, d=128: full oracle
     case(4, 16, 16, 2048, 128, torch.bfloat16, True, seed=2)
