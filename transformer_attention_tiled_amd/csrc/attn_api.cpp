@@ -140,7 +140,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
       overlap(lse, lbytes, k, kvbytes) || overlap(lse, lbytes, v, kvbytes) ||
       overlap(lse, lbytes, o, qbytes))
     return ATTN_ERR_SHAPE;
-  // query tiles of 64 (fp32) or 128 (bf16) rows, all in one grid dimension
+  // query tiles of 64 (fp32) or 256 (bf16) rows, all in one grid dimension;
+  // the bound takes the smaller tile
   int64_t grid;
   if (!mul({((int64_t)T + 63) / 64, B, Hq}, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
 
