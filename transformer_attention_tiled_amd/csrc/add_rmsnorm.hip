@@ -16,6 +16,11 @@
 // every load and store is a whole 16-byte vector and the 256 threads cover
 // consecutive 4 KiB spans. The row's sum of squares is reduced within each
 // wave by lane exchanges, then across the 4 waves through LDS.
+//
+// Both outputs are written with a streaming (non-temporal) hint: they are
+// not read again by this kernel, and without the hint the writes sit dirty
+// in the caches and compete with the reads (measured at 4096 x 4096: 26.1 us
+// plain, 21.1 us with the hint; non-temporal loads as well: 24.3 us).
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -72,7 +77,8 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(NormArgs a) {
         ss = __builtin_fmaf(h[i][2 * q + 1], h[i][2 * q + 1], ss);
         hv[q] = pack_bf16(h[i][2 * q], h[i][2 * q + 1]);
       }
-      h_out[c] = hv;  // the same thread read this chunk of residual above
+      // the same thread read this chunk of residual above (in-place update)
+      __builtin_nontemporal_store(hv, h_out + c);
     }
   }
   // row sum of squares: lanes, then waves
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(NormArgs a) {
       for (int q = 0; q < 4; ++q)
         yv[q] = pack_bf16(h[i][2 * q] * inv * bf16_lo(wv[q]),
                           h[i][2 * q + 1] * inv * bf16_hi(wv[q]));
-      y_out[c] = yv;
+      __builtin_nontemporal_store(yv, y_out + c);
     }
   }
 }

@@ -23,7 +23,10 @@
 // finds each row's sequence (binary search over query_start_loc, staged in
 // LDS), position and physical block, then issues the stores. Each byte is
 // read once and written once: the kernel is bound by HBM bandwidth and
-// latency (it does no arithmetic).
+// latency (it does no arithmetic). The cache writes carry a streaming
+// (non-temporal) hint, so they do not sit dirty in the caches while the
+// reads stream (mixed-batch shape, 4352 rows x Hkv 8: 8.05 us plain, 6.99 us
+// with the hint).
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -114,8 +117,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         const int g = gc / CH;
         const int64_t rb = row_base[ti];
         if (rb >= 0)
-          *(u32x4*)((is_v ? vc : kc) + rb + (int64_t)g * (kBlockSize - 1) * D + (int64_t)gc * 8) =
-              val[u];
+          __builtin_nontemporal_store(
+              val[u],
+              (u32x4*)((is_v ? vc : kc) + rb + (int64_t)g * (kBlockSize - 1) * D + (int64_t)gc * 8));
       }
     }
   }
