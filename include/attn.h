@@ -43,10 +43,12 @@
  *  - bf16 is IEEE bfloat16 (the upper 16 bits of an fp32). Products are
  *    accumulated in fp32. The bf16 paths fold the softmax scale into the
  *    query: each element of q is multiplied by scale * log2(e) (fp32) and
- *    rounded to bf16 once, so the scores carry that one extra rounding
- *    (relative 2^-9 per element of q). The softmax weights are rounded to
- *    bf16 (round-to-nearest-even) before the product with V, their row sum
- *    is taken in fp32 from the unrounded weights, and outputs are rounded to
+ *    rounded to bf16 once (round-to-nearest-even: a relative error of at
+ *    most 2^-8 per element of q), so a score q.k moves by at most
+ *    2^-8 * scale * sum_i |q_i k_i| and lse by at most the largest such move
+ *    over the keys the row sees. The softmax weights are rounded to bf16
+ *    (round-to-nearest-even) before the product with V, their row sum is
+ *    taken in fp32 from the unrounded weights, and outputs are rounded to
  *    the output type at the end. The fp32 prefill path rounds nothing.
  *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
  *  - `scale` multiplies the scores before the softmax; it must be finite and

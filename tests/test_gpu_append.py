@@ -101,10 +101,10 @@ def test_append_then_decode_step():
                               b["seq_lens"])
     rk = torch.from_numpy(rk).view(torch.bfloat16)
     rv = torch.from_numpy(rv).view(torch.bfloat16)
-    ro, rl = ref_decode(b["q"], rk, rv, b["block_table"], b["seq_lens"],
+    ro, rl, rb = ref_decode(b["q"], rk, rv, b["block_table"], b["seq_lens"],
                                  1.0 / math.sqrt(128))
     assert_close(o, ro, torch.bfloat16, "append + decode")
-    assert_lse_close(lse, rl, "append + decode")
+    assert_lse_close(lse, rl, rb, "append + decode")
 
 
 def test_append_full_size_mixed_batch_sampled():

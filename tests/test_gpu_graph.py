@@ -99,11 +99,11 @@ def test_captured_decode_step_replays_match_eager_and_oracle():
         seq_lens = torch.tensor(lens, dtype=torch.int32)
         rk, rv = oracle.kv_append(kn.cpu(), vn.cpu(), kc_before.cpu(), vc_before.cpu(), table,
                                   seq_lens)
-        ro, rl = ref_decode(static["q"].cpu(), torch.from_numpy(rk).view(torch.bfloat16),
+        ro, rl, rb = ref_decode(static["q"].cpu(), torch.from_numpy(rk).view(torch.bfloat16),
                                      torch.from_numpy(rv).view(torch.bfloat16), table, seq_lens,
                                      1.0 / math.sqrt(d))
         assert_close(o_g, ro, torch.bfloat16, f"graph replay {rep}")
-        assert_lse_close(lse_g, rl, f"graph replay {rep}")
+        assert_lse_close(lse_g, rl, rb, f"graph replay {rep}")
 
 
 def test_captured_prefill_replays_match_eager():
@@ -139,6 +139,6 @@ def test_captured_prefill_replays_match_eager():
         assert torch.equal(lse_g, lse), f"replay {rep}: lse differs from the eager call"
         del junk
         if rep == 0:  # and once against the oracle, on two heads
-            ro, rl = ref_prefill(qn, kn, vn, 1.0 / math.sqrt(d), causal=True, heads=[0, 5])
+            ro, rl, rb = ref_prefill(qn, kn, vn, 1.0 / math.sqrt(d), causal=True, heads=[0, 5])
             assert_close(o_g[:, [0, 5]], ro[:, [0, 5]], torch.bfloat16, "graph prefill")
-            assert_lse_close(lse_g[:, [0, 5]], rl[:, [0, 5]], "graph prefill lse")
+            assert_lse_close(lse_g[:, [0, 5]], rl[:, [0, 5]], rb[:, [0, 5]], "graph prefill lse")

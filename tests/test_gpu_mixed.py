@@ -37,11 +37,11 @@ def test_small_mixed_with_context(seed):
     print(f"[mixed] small seed={seed}", flush=True)
     b = inputs.paged_inputs(len(seq_lens), 8, 2, 128, seq_lens=seq_lens, q_lens=q_lens, seed=seed)
     o, lse = run(b)
-    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+    ro, rl, rb = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
                                  b["seq_lens"], 1.0 / math.sqrt(128),
                                  query_start_loc=b["query_start_loc"])
     assert_close(o, ro, torch.bfloat16, "mixed")
-    assert_lse_close(lse, rl, "mixed")
+    assert_lse_close(lse, rl, rb, "mixed")
 
 
 def test_growing_scores_paged_chunks_and_decodes():
@@ -65,10 +65,10 @@ def test_growing_scores_paged_chunks_and_decodes():
             kc[blk, :, p % 16, :] = 0.1 * kc[blk, :, p % 16, :] + a * (p / 64.0)
     b["k_cache"] = kc.to(torch.bfloat16)
     o, lse = run(b)
-    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+    ro, rl, rb = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
                         1.0 / math.sqrt(d), query_start_loc=b["query_start_loc"])
     assert_close(o, ro, torch.bfloat16, "growing scores, paged")
-    assert_lse_close(lse, rl, "growing scores, paged")
+    assert_lse_close(lse, rl, rb, "growing scores, paged")
 
 
 def test_mixed_d64_gqa4():
@@ -76,11 +76,11 @@ def test_mixed_d64_gqa4():
     q_lens = [128, 1, 200]
     b = inputs.paged_inputs(3, 16, 4, 64, seq_lens=seq_lens, q_lens=q_lens, seed=72)
     o, lse = run(b)
-    ro, rl = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
+    ro, rl, rb = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"],
                                  b["seq_lens"], 1.0 / math.sqrt(64),
                                  query_start_loc=b["query_start_loc"])
     assert_close(o, ro, torch.bfloat16, "mixed d64")
-    assert_lse_close(lse, rl, "mixed d64")
+    assert_lse_close(lse, rl, rb, "mixed d64")
 
 
 def test_chunk_rows_match_contiguous_prefill():
@@ -118,11 +118,38 @@ def test_mixed_many_sequences_direct_grid():
     dec = sorted(set(int(x) for x in rng.choice(2100, 40, replace=False)) - set(chunks))
     seqs = chunks + dec
     kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
-    ro, rl = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(64), query_start_loc=qsl_c)
+    ro, rl, rb = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(64), query_start_loc=qsl_c)
     qsl = b["query_start_loc"]
     rows = torch.cat([torch.arange(int(qsl[n]), int(qsl[n + 1])) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "2100 sequences")
-    assert_lse_close(lse[rows.to(DEV)], rl, "2100 sequences")
+    assert_lse_close(lse[rows.to(DEV)], rl, rb, "2100 sequences")
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 1)])
+def test_mixed_many_chunk_sequences_persistent_unsorted(d, Hq, Hkv):
+    # 200 chunk sequences (more than the 128 that the persistent chunk kernel
+    # orders by length) among 800 sequences (within the 2048 it stages): the
+    # persistent kernel then takes the chunk items in batch order. Chunks and
+    # decodes interleave in the batch, chunks have ragged lengths and prior
+    # context; every chunk and 40 decodes are checked against the oracle.
+    print(f"[mixed] 800 sequences, 200 chunks, d={d}", flush=True)
+    rng = np.random.default_rng(74 + d)
+    n = 800
+    chunk_ids = sorted(int(x) for x in rng.choice(n, 200, replace=False))
+    q_lens = [1] * n
+    for c in chunk_ids:
+        q_lens[c] = int(rng.integers(2, 301))
+    seq_lens = [q + int(rng.integers(0, 201)) for q in q_lens]
+    b = inputs.paged_inputs(n, Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens, seed=74 + d)
+    o, lse = run(b)
+    dec = sorted(set(int(x) for x in rng.choice(n, 60, replace=False)) - set(chunk_ids))[:40]
+    seqs = chunk_ids + dec
+    kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
+    ro, rl, rb = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(d), query_start_loc=qsl_c)
+    qsl = b["query_start_loc"]
+    rows = torch.cat([torch.arange(int(qsl[m]), int(qsl[m + 1])) for m in seqs])
+    assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "200 chunk sequences")
+    assert_lse_close(lse[rows.to(DEV)], rl, rb, "200 chunk sequences")
 
 
 def test_config_mixed_batch_full_size_sampled():
@@ -145,11 +172,11 @@ def test_config_mixed_batch_full_size_sampled():
     pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
     seqs = list(range(8)) + sorted(pick)
     kc, vc, table, sl, q, qsl = inputs.compact_sequences(b, seqs)
-    ro, rl = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl)
+    ro, rl, rb = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl)
     qsl_full = b["query_start_loc"].cpu()
     rows = torch.cat([torch.arange(int(qsl_full[n]), int(qsl_full[n + 1])) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "full-size mixed")
-    assert_lse_close(lse[rows.to(DEV)], rl, "full-size mixed")
+    assert_lse_close(lse[rows.to(DEV)], rl, rb, "full-size mixed")
     del b
     torch.cuda.empty_cache()
 
@@ -184,19 +211,19 @@ def test_config_mixed_batch_with_context_full_size_sampled():
         V = oracle.gather_paged_kv(vc, table[0].numpy(), L).transpose(1, 0, 2)[None]
         Q = np.zeros((1, 32, L, 128))
         Q[0, :, ctx:] = q.double().numpy().transpose(1, 0, 2)
-        ro, rl = ref_prefill(Q, K, V, scale, causal=True, rows=[ctx + i for i in picks])
+        ro, rl, rb = ref_prefill(Q, K, V, scale, causal=True, rows=[ctx + i for i in picks])
         rows = torch.tensor([int(qsl[n]) + i for i in picks])
         got = o[rows.to(DEV)].transpose(0, 1)  # [Hq, rows, d]
         assert_close(got, ro[0], torch.bfloat16, f"chunk {n} (context {ctx})")
-        assert_lse_close(lse[rows.to(DEV)].transpose(0, 1), rl[0], f"chunk {n} lse")
+        assert_lse_close(lse[rows.to(DEV)].transpose(0, 1), rl[0], rb[0], f"chunk {n} lse")
     dec = list(range(8, 264))
     pick = {min(dec, key=lambda n: lens[n]), max(dec, key=lambda n: lens[n])}
     pick |= set(int(x) for x in rng.choice(dec, 14, replace=False))
     seqs = sorted(pick)
     kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
-    ro, rl = ref_decode(q, kc, vc, table, sl, scale, query_start_loc=qsl_c)
+    ro, rl, rb = ref_decode(q, kc, vc, table, sl, scale, query_start_loc=qsl_c)
     rows = torch.tensor([int(qsl[n]) for n in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "decodes next to context chunks")
-    assert_lse_close(lse[rows.to(DEV)], rl, "decodes next to context chunks")
+    assert_lse_close(lse[rows.to(DEV)], rl, rb, "decodes next to context chunks")
     del b
     torch.cuda.empty_cache()

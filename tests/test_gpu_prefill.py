@@ -10,7 +10,7 @@ import torch
 import oracle
 import transformer_attention_tiled_amd as attn
 from transformer_attention_tiled_amd import inputs
-from parity import assert_close, assert_lse_close, ref_prefill
+from parity import F32_MAX_ABS, assert_close, assert_lse_close, ref_prefill
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -31,10 +31,13 @@ def case(B, Hq, Hkv, T, d, dtype, causal, seed):
     sys.stdout.flush()
     q, k, v = inputs.prefill_inputs(B, Hq, Hkv, T, d, dtype, seed=seed)
     o, lse = run(q, k, v, causal)
-    ref = ref_prefill if dtype == torch.bfloat16 else oracle.prefill
-    ref_o, ref_lse = ref(q, k, v, 1.0 / math.sqrt(d), causal=causal)
+    if dtype == torch.bfloat16:
+        ref_o, ref_lse, bound = ref_prefill(q, k, v, 1.0 / math.sqrt(d), causal=causal)
+    else:  # the fp32 path rounds nothing
+        ref_o, ref_lse = oracle.prefill(q, k, v, 1.0 / math.sqrt(d), causal=causal)
+        bound = F32_MAX_ABS
     assert_close(o, ref_o, dtype, f"T={T} d={d}")
-    assert_lse_close(lse, ref_lse, f"T={T} d={d}")
+    assert_lse_close(lse, ref_lse, bound, f"T={T} d={d}")
 
 
 def test_config_fp32_small():
@@ -81,21 +84,19 @@ def test_config_bf16_b4_t2048():
     case(4, 16, 16, 2048, 128, torch.bfloat16, True, seed=2)
 
 
-def test_config_bf16_gqa_t16384_sampled():
-    # B=1, Hq=32, Hkv=8, T=16384, d=128: heads at group boundaries, sampled rows
-    print("[prefill] long GQA config T=16384", flush=True)
+def test_config_bf16_gqa_t16384_heads():
+    # B=1, Hq=32, Hkv=8, T=16384, d=128: every one of the 16384 rows of query
+    # heads 0, 3, 4 and 31 (two GQA group boundaries and the last group)
+    # against the oracle; the remaining heads are checked for finiteness
+    print("[prefill] long GQA config T=16384, heads 0 3 4 31, all rows", flush=True)
     q, k, v = inputs.prefill_inputs(1, 32, 8, 16384, 128, torch.bfloat16, seed=3)
     o, lse = run(q, k, v, True)
-    rng = np.random.default_rng(3)
-    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 4095, 8191, 8192, 16256, 16383] +
-                      rng.integers(0, 16384, 36).tolist()))
     heads = [0, 3, 4, 31]
-    ref_o, ref_lse = ref_prefill(q, k, v, 1.0 / math.sqrt(128), causal=True, rows=rows,
-                                 heads=heads)
-    got = o[:, heads][:, :, rows]
-    assert_close(got, ref_o[:, heads], torch.bfloat16, "T=16384 sampled")
-    assert_lse_close(lse[:, heads][:, :, rows], ref_lse[:, heads], "T=16384 sampled")
-    assert torch.isfinite(o).all()
+    ref_o, ref_lse, bound = ref_prefill(q, k, v, 1.0 / math.sqrt(128), causal=True, heads=heads)
+    mx, mean = assert_close(o[:, heads], ref_o[:, heads], torch.bfloat16, "T=16384")
+    lmx = assert_lse_close(lse[:, heads], ref_lse[:, heads], bound[:, heads], "T=16384 lse")
+    print(f"[prefill] T=16384: o max {mx:.3e} mean {mean:.3e}, lse max {lmx:.3e}", flush=True)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
 def test_causality_is_exact():
@@ -155,9 +156,9 @@ def test_running_max_moves_on_most_tiles(d):
     k = (0.1 * torch.randn(B, Hkv, T, d, generator=g) + a * ramp).to(torch.bfloat16)
     v = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
     o, lse = run(q, k, v, True)
-    ref_o, ref_lse = ref_prefill(q, k, v, 1.0 / math.sqrt(d), causal=True)
+    ref_o, ref_lse, bound = ref_prefill(q, k, v, 1.0 / math.sqrt(d), causal=True)
     assert_close(o, ref_o, torch.bfloat16, f"growing scores d={d}")
-    assert_lse_close(lse, ref_lse, f"growing scores d={d}")
+    assert_lse_close(lse, ref_lse, bound, f"growing scores d={d}")
 
 
 def test_rejects_unsupported_without_fallback():
