@@ -73,7 +73,8 @@ enum {
   ATTN_ERR_UNSUPPORTED = -3, /* valid request outside the supported set */
   ATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_WORKSPACE = -5,   /* workspace missing or too small */
-  ATTN_ERR_LAUNCH = -6       /* the HIP runtime rejected a launch */
+  ATTN_ERR_LAUNCH = -6,      /* the HIP runtime rejected a launch */
+  ATTN_ERR_SCRATCH = -7      /* the no-allocation variant's fixed scratch is too small */
 };
 
 /*
@@ -167,6 +168,32 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int max_query_len, int64_t num_blocks, float scale,
                       attn_dtype dtype, int partition_size, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc — attn_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. It allocates nothing and takes no
+ * workspace argument: the split-KV partials live in a fixed array inside the
+ * library, ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends. Arguments,
+ * layouts, results and errors are those of attn_decode_paged (same kernels,
+ * bitwise the same output for the same partition size), plus:
+ *   - ATTN_ERR_SCRATCH when the request needs more than the fixed array
+ *     (attn_decode_paged_workspace_size(...) > ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+ *     nothing is launched then.
+ *   - ATTN_ERR_LAUNCH if the array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and must not be made.
+ * Calls on the same stream are ordered and safe.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, void* o,
+                              int num_seqs, int num_tokens, int Hq, int Hkv, int d,
+                              int block_size, int max_blocks_per_seq, int max_seq_len,
+                              int max_query_len, int64_t num_blocks, float scale,
+                              attn_dtype dtype, int partition_size, float* lse, void* stream);
 
 /*
  * attn_kv_append — write the new tokens' keys and values into a paged KV

@@ -189,3 +189,38 @@ def add_rmsnorm(lib, x=P, r=P2, w=P3, out=P4, rout=P4 + 0x10000000, rows=4, hidd
 ])
 def test_add_rmsnorm_rejects(lib, kw, code):
     assert add_rmsnorm(lib, **kw) == code
+
+
+def decode_noalloc(lib, q=P, kc=P2, vc=P3, table=P4, seq_lens=P4 + 0x40000000, qsl=None,
+                   o=P4 + 0x50000000, num_seqs=4, num_tokens=4, Hq=8, Hkv=2, d=128,
+                   block_size=16, mbps=8, max_seq_len=128, max_query_len=1, num_blocks=64,
+                   scale=0.088, dtype=BF16, partition_size=0, lse=None):
+    return lib.attn_decode_paged_noalloc(q, kc, vc, table, seq_lens, qsl, o, num_seqs,
+                                         num_tokens, Hq, Hkv, d, block_size, mbps, max_seq_len,
+                                         max_query_len, num_blocks, ctypes.c_float(scale), dtype,
+                                         partition_size, lse, None)
+
+
+SCRATCH = -7
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(table=None), NULL),
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(block_size=8), UNSUP),
+    (dict(Hq=7), SHAPE), (dict(max_seq_len=0), SHAPE), (dict(mbps=7), SHAPE),
+    (dict(q=P + 8), ALIGN),
+    (dict(o=P), SHAPE),                                  # output over q
+    # 2000 sequences of 32768 tokens in 16-token partitions: far beyond the
+    # fixed array, refused before the array's address is even looked up
+    (dict(num_seqs=2000, num_tokens=2000, Hq=32, Hkv=8, mbps=2048, max_seq_len=32768,
+          partition_size=16, seq_lens=P4 + 0x60000000, o=P4 + 0x70000000), SCRATCH),
+])
+def test_decode_noalloc_rejects_on_the_host(lib, kw, code):
+    assert decode_noalloc(lib, **kw) == code
+
+
+def test_noalloc_limit_matches_header(lib):
+    text = open(HEADER).read()
+    assert "ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert attn.DECODE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert attn.status_string(SCRATCH) != "unknown status"

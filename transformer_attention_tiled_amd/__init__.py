@@ -10,6 +10,8 @@ from ._binding import (  # noqa: F401
     AttnError,
     prefill,
     decode_paged,
+    decode_paged_noalloc,
+    DECODE_NOALLOC_SCRATCH_BYTES,
     decode_paged_workspace_size,
     decode_paged_partition_size,
     kv_append,

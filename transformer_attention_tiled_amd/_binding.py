@@ -27,7 +27,11 @@ _STATUS_NAMES = {
     -4: "ATTN_ERR_ALIGN",
     -5: "ATTN_ERR_WORKSPACE",
     -6: "ATTN_ERR_LAUNCH",
+    -7: "ATTN_ERR_SCRATCH",
 }
+
+# bytes of the fixed device array behind decode_paged_noalloc (include/attn.h)
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class AttnError(RuntimeError):
@@ -72,6 +76,8 @@ def load_library():
                                       c_int, c_int, c_int, c_int, ctypes.c_int64, c_float,
                                       c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.attn_decode_paged.restype = c_int
+    lib.attn_decode_paged_noalloc.argtypes = lib.attn_decode_paged.argtypes[:-3] + [c_void_p]
+    lib.attn_decode_paged_noalloc.restype = c_int
     lib.attn_kv_append.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                    ctypes.c_int64, c_int, c_void_p]
@@ -246,6 +252,32 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, max
         _dtype_code(q.dtype), int(partition_size), _ptr(lse), _ptr(workspace), ws_have,
         _stream(dev))
     _check(status, "attn_decode_paged")
+    return o
+
+
+def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, *, max_seq_len,
+                         max_query_len=1, query_start_loc=None, scale=None, partition_size=0,
+                         lse=None):
+    """attn_decode_paged_noalloc: decode_paged with no allocation at all, for
+    callers that cannot allocate (graph capture, tight serving loops). The
+    caller passes the output ``o``; the split-KV partials go to the library's
+    fixed per-GPU array of DECODE_NOALLOC_SCRATCH_BYTES. Calls that overlap in
+    time on one GPU race (they share that array). Returns o."""
+    A = _Args("decode_paged_noalloc")
+    num_tokens, Hq, d, num_blocks, Hkv, block_size, num_seqs = _paged_common(
+        A, q, k_cache, v_cache, block_table, seq_lens, query_start_loc)
+    A.tensor("o", o, dtype=q.dtype, shape=q.shape)
+    A.tensor("lse", lse, dtype=torch.float32, shape=(num_tokens, Hq), optional=True)
+    dev = A.devices()
+    lib = load_library()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    status = lib.attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(query_start_loc), _ptr(o), num_seqs, num_tokens, Hq, Hkv, d, block_size,
+        block_table.shape[1], int(max_seq_len), int(max_query_len), num_blocks, float(scale),
+        _dtype_code(q.dtype), int(partition_size), _ptr(lse), _stream(dev))
+    _check(status, "attn_decode_paged_noalloc")
     return o
 
 

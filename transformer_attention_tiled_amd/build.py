@@ -20,6 +20,7 @@ OUT = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
+           "decode_noalloc.hip",
            "kv_append.hip", "add_rmsnorm.hip"]
 
 COMMON = [

@@ -102,6 +102,95 @@ int device_cu_count() {
   return cu;
 }
 
+// Validation, then launch, of one paged call. The workspace is either the
+// caller's (workspace, workspace_bytes) or, when `scratch` is given, asked
+// of it only after every check has passed, so that a rejected request makes
+// no HIP call at all.
+int decode_paged_run(const DecodeRequest& r, void* workspace, size_t workspace_bytes,
+                     ScratchProvider scratch, void* stream) {
+  const void *q = r.q, *k_cache = r.k_cache, *v_cache = r.v_cache;
+  const int32_t *block_table = r.block_table, *seq_lens = r.seq_lens,
+                *query_start_loc = r.query_start_loc;
+  void* o = r.o;
+  float* lse = r.lse;
+  const int num_seqs = r.num_seqs, num_tokens = r.num_tokens, Hq = r.Hq, Hkv = r.Hkv, d = r.d;
+  const int max_blocks_per_seq = r.max_blocks_per_seq, max_seq_len = r.max_seq_len,
+            max_query_len = r.max_query_len, partition_size = r.partition_size;
+  const int64_t num_blocks = r.num_blocks;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || o == nullptr)
+    return ATTN_ERR_NULL;
+  if (r.dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || num_tokens < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!supported_d(d) || r.block_size != kBlockSize || Hq / Hkv > 16 || !good_scale(r.scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (max_seq_len < 1 || num_blocks < 1 || max_query_len < 1 || max_query_len > max_seq_len ||
+      max_query_len > num_tokens)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq < ((int64_t)max_seq_len + kBlockSize - 1) / kBlockSize)
+    return ATTN_ERR_SHAPE;
+  if (query_start_loc == nullptr && (max_query_len != 1 || num_tokens < num_seqs))
+    return ATTN_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % kBlockSize != 0) return ATTN_ERR_SHAPE;
+  if (partition_size > kMaxPartition) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4) ||
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return ATTN_ERR_ALIGN;
+  WsLayout w;
+  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
+  if (scratch == nullptr && (workspace == nullptr || workspace_bytes < w.total))
+    return ATTN_ERR_WORKSPACE;
+  if (scratch != nullptr && w.total > kNoAllocScratchBytes) return ATTN_ERR_SCRATCH;
+  int64_t qb, cb, tb, lb;
+  if (!mul({num_tokens, Hq, d, 2}, &qb) || !mul({num_blocks, Hkv, kBlockSize, d, 2}, &cb) ||
+      !mul({num_seqs, max_blocks_per_seq, 4}, &tb) || !mul({num_tokens, Hq, 4}, &lb))
+    return ATTN_ERR_SHAPE;
+  {
+    // what the call writes (o, lse, the workspace) overlaps nothing it reads
+    // and no other output (the library's own scratch array is a separate
+    // allocation and overlaps nothing of the caller's)
+    const void* in[] = {q, k_cache, v_cache, block_table, seq_lens, query_start_loc};
+    const int64_t in_bytes[] = {qb, cb, cb, tb, (int64_t)num_seqs * 4,
+                                (int64_t)(num_seqs + 1) * 4};
+    const void* out[] = {o, lse, scratch != nullptr ? nullptr : workspace};
+    const int64_t out_bytes[] = {qb, lb, (int64_t)w.total};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 6; ++j)
+        if (overlap(out[i], out_bytes[i], in[j], in_bytes[j])) return ATTN_ERR_SHAPE;
+      for (int j = i + 1; j < 3; ++j)
+        if (overlap(out[i], out_bytes[i], out[j], out_bytes[j])) return ATTN_ERR_SHAPE;
+    }
+  }
+  int64_t g1, g2;
+  const int64_t n_qt = ((int64_t)max_query_len + 255) / 256;  // 256-row query tiles
+  if (!mul({w.max_parts, Hkv, num_seqs}, &g1) || g1 > kMaxGrid ||
+      !mul({n_qt, num_seqs, Hq}, &g2) || g2 > kMaxGrid)
+    return ATTN_ERR_SHAPE;
+
+  // every check has passed: only now may the scratch provider touch HIP
+  if (scratch != nullptr) {
+    const int st = scratch(&workspace);
+    if (st != ATTN_OK) return st;
+  }
+  PagedArgs a;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.qsl = query_start_loc;
+  a.o = o; a.lse = lse;
+  a.num_seqs = num_seqs; a.num_tokens = num_tokens; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+  a.max_blocks_per_seq = max_blocks_per_seq; a.max_seq_len = max_seq_len;
+  a.max_query_len = max_query_len; a.num_blocks = num_blocks; a.scale = r.scale;
+  a.partition_size = w.partition_size; a.max_parts = w.max_parts;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_query_len >= 2) {
+    if (launch_paged_prefill_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  if (launch_paged_decode_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return ATTN_OK;
+}
+
 }  // namespace attn
 
 extern "C" {
@@ -115,6 +204,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGN: return "a pointer is not aligned as required";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case ATTN_ERR_SCRATCH:
+      return "the request needs more scratch memory than the fixed no-allocation array holds";
     default: return "unknown status";
   }
 }
@@ -174,70 +265,10 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int max_seq_len, int max_query_len, int64_t num_blocks, float scale,
                       attn_dtype dtype, int partition_size, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
-      seq_lens == nullptr || o == nullptr)
-    return ATTN_ERR_NULL;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (num_seqs < 1 || num_tokens < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  if (!supported_d(d) || block_size != attn::kBlockSize || Hq / Hkv > 16 || !good_scale(scale))
-    return ATTN_ERR_UNSUPPORTED;
-  if (max_seq_len < 1 || num_blocks < 1 || max_query_len < 1 || max_query_len > max_seq_len ||
-      max_query_len > num_tokens)
-    return ATTN_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq < ((int64_t)max_seq_len + attn::kBlockSize - 1) / attn::kBlockSize)
-    return ATTN_ERR_SHAPE;
-  if (query_start_loc == nullptr && (max_query_len != 1 || num_tokens < num_seqs))
-    return ATTN_ERR_SHAPE;
-  if (partition_size < 0 || partition_size % attn::kBlockSize != 0) return ATTN_ERR_SHAPE;
-  if (partition_size > attn::kMaxPartition) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4) ||
-      !aligned(lse, 4) || !aligned(workspace, 256))
-    return ATTN_ERR_ALIGN;
-  WsLayout w;
-  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
-  if (workspace == nullptr || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
-  {
-    // what the call writes (o, lse, the workspace) overlaps nothing it reads
-    // and no other output
-    int64_t qb, cb, tb, lb;
-    if (!mul({num_tokens, Hq, d, 2}, &qb) || !mul({num_blocks, Hkv, attn::kBlockSize, d, 2}, &cb) ||
-        !mul({num_seqs, max_blocks_per_seq, 4}, &tb) || !mul({num_tokens, Hq, 4}, &lb))
-      return ATTN_ERR_SHAPE;
-    const void* in[] = {q, k_cache, v_cache, block_table, seq_lens, query_start_loc};
-    const int64_t in_bytes[] = {qb, cb, cb, tb, (int64_t)num_seqs * 4,
-                                (int64_t)(num_seqs + 1) * 4};
-    const void* out[] = {o, lse, workspace};
-    const int64_t out_bytes[] = {qb, lb, (int64_t)w.total};
-    for (int i = 0; i < 3; ++i) {
-      for (int j = 0; j < 6; ++j)
-        if (overlap(out[i], out_bytes[i], in[j], in_bytes[j])) return ATTN_ERR_SHAPE;
-      for (int j = i + 1; j < 3; ++j)
-        if (overlap(out[i], out_bytes[i], out[j], out_bytes[j])) return ATTN_ERR_SHAPE;
-    }
-  }
-  int64_t g1, g2;
-  const int64_t n_qt = ((int64_t)max_query_len + 255) / 256;  // 256-row query tiles
-  if (!mul({w.max_parts, Hkv, num_seqs}, &g1) || g1 > kMaxGrid ||
-      !mul({n_qt, num_seqs, Hq}, &g2) || g2 > kMaxGrid)
-    return ATTN_ERR_SHAPE;
-
-  attn::PagedArgs a;
-  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
-  a.block_table = block_table; a.seq_lens = seq_lens; a.qsl = query_start_loc;
-  a.o = o; a.lse = lse;
-  a.num_seqs = num_seqs; a.num_tokens = num_tokens; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
-  a.max_blocks_per_seq = max_blocks_per_seq; a.max_seq_len = max_seq_len;
-  a.max_query_len = max_query_len; a.num_blocks = num_blocks; a.scale = scale;
-  a.partition_size = w.partition_size; a.max_parts = w.max_parts;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (max_query_len >= 2) {
-    if (attn::launch_paged_prefill_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
-  }
-  if (attn::launch_paged_decode_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
-  return ATTN_OK;
+  attn::DecodeRequest r{q, k_cache, v_cache, block_table, seq_lens, query_start_loc, o, lse,
+                        num_seqs, num_tokens, Hq, Hkv, d, block_size, max_blocks_per_seq,
+                        max_seq_len, max_query_len, num_blocks, scale, dtype, partition_size};
+  return attn::decode_paged_run(r, workspace, workspace_bytes, nullptr, stream);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

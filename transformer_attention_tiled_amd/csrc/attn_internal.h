@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/attn.h"
+
 namespace attn {
 
 // Contiguous prefill: q,o [B][Hq][T][d], k,v [B][Hkv][T][d].
@@ -74,6 +76,36 @@ int device_cu_count();
 
 // Host-side policy shared by the workspace query and the launch.
 int decode_partition_size(int num_seqs, int Hkv, int max_seq_len);
+
+// One attn_decode_paged request as the caller made it (before validation).
+struct DecodeRequest {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  void* o;
+  float* lse;
+  int num_seqs, num_tokens, Hq, Hkv, d, block_size, max_blocks_per_seq, max_seq_len,
+      max_query_len;
+  int64_t num_blocks;
+  float scale;
+  attn_dtype dtype;
+  int partition_size;
+};
+
+// Bytes of the fixed device array behind attn_decode_paged_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+// Supplies the device address of the library's scratch array on the current
+// device (ATTN_OK) or a failure status. Called only after validation passed.
+typedef int (*ScratchProvider)(void** ptr);
+
+// Validate a paged request, then launch it with the caller's workspace, or
+// with the scratch array when `scratch` is not null.
+int decode_paged_run(const DecodeRequest& r, void* workspace, size_t workspace_bytes,
+                     ScratchProvider scratch, void* stream);
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
