@@ -86,6 +86,24 @@ bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partit
 
 namespace attn {
 
+int decode_partition_size(int num_seqs, int Hkv, int max_seq_len) {
+  if (num_seqs < 1 || Hkv < 1 || max_seq_len < 1) return 0;
+  // One wave per partition, up to six resident per CU, all resident from the
+  // start. Aim for about 608 partitions (2.4 per CU of 256): on MI355X fewer,
+  // longer partitions beat more, shorter ones until about that point (64
+  // sequences, Hkv 2, lengths up to 4096: 37.0-37.5 us at 416..464-token
+  // partitions, 40.8 us at 272, 39.6 us at 512). The mean length is
+  // estimated as half the maximum; partitions stay between 256 and 4096
+  // tokens, in whole 16-token blocks.
+  constexpr int64_t kTargetParts = 608;
+  const int64_t units = (int64_t)num_seqs * Hkv;
+  int64_t P = (units * ((int64_t)max_seq_len / 2 + 1) + kTargetParts - 1) / kTargetParts;
+  if (P < 256) P = 256;
+  if (P > kMaxPartition) P = kMaxPartition;
+  P = (P + 15) / 16 * 16;
+  return (int)P;
+}
+
 int device_cu_count() {
   constexpr int kMaxDevices = 64;
   // 0: not queried yet; threads that race both store the same value

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/attn.h"
+#include "paged_index.h"
 
 namespace attn {
 
@@ -111,7 +112,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s);  // q_len >= 2 sequences
 hipError_t launch_paged_decode_bf16(const PagedArgs& a, hipStream_t s);   // q_len == 1 sequences
-int append_grid(int num_tokens);  // workgroups of the append launch
+constexpr int kAppendRows = 8;  // new rows per workgroup of the append kernel
+inline int append_grid(int num_tokens) { return (num_tokens + kAppendRows - 1) / kAppendRows; }
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_add_rmsnorm_bf16(const NormArgs& a, hipStream_t s);
 

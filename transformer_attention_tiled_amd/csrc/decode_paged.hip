@@ -240,20 +240,18 @@ __global__ __launch_bounds__(64) void decode_kernel(PagedArgs a, float c) {
   // on, the only outstanding loads are the ring copies, counted exactly.
   __builtin_amdgcn_s_waitcnt(0);
 
-  const int64_t bstride = (int64_t)a.Hkv * kBlockSize * D;
-  const uint16_t* kbase = (const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D;
-  const uint16_t* vbase = (const uint16_t*)a.v_cache + (int64_t)g * kBlockSize * D;
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
 
-  auto phys_of = [&](int b) -> int64_t {
+  // element offset of block b's (block, head g) rows in the caches
+  auto offset_of = [&](int b) -> int64_t {
     const int j = b >> 6;
     const int v = j == 0 ? tbl[0] : j == 1 ? tbl[1] : j == 2 ? tbl[2] : tbl[3];
-    return __builtin_amdgcn_readlane(v, b & 63);
+    return paged_kv_offset(__builtin_amdgcn_readlane(v, b & 63), g, a.Hkv, D);
   };
   auto issue = [&](int b) {
-    const int64_t phys = phys_of(b);
-    issue_block<D>(kbase + phys * bstride, vbase + phys * bstride, min(16, end - (start + 16 * b)),
-                   ring0 + (b % kRing) * C::SLOT, lane);
+    const int64_t off = offset_of(b);
+    issue_block<D>((const uint16_t*)a.k_cache + off, (const uint16_t*)a.v_cache + off,
+                   min(16, end - (start + 16 * b)), ring0 + (b % kRing) * C::SLOT, lane);
   };
 
   f32x4 acc[DPL];
@@ -475,24 +473,6 @@ __global__ __launch_bounds__(256) void decode_merge_loop_kernel(PagedArgs a) {
 }
 
 }  // namespace
-
-int decode_partition_size(int num_seqs, int Hkv, int max_seq_len) {
-  if (num_seqs < 1 || Hkv < 1 || max_seq_len < 1) return 0;
-  // One wave per partition, up to six resident per CU, all resident from the
-  // start. Aim for about 608 partitions (2.4 per CU of 256): on MI355X fewer,
-  // longer partitions beat more, shorter ones until about that point (64
-  // sequences, Hkv 2, lengths up to 4096: 37.0-37.5 us at 416..464-token
-  // partitions, 40.8 us at 272, 39.6 us at 512). The mean length is
-  // estimated as half the maximum; partitions stay between 256 and 4096
-  // tokens, in whole 16-token blocks.
-  constexpr int64_t kTargetParts = 608;
-  const int64_t units = (int64_t)num_seqs * Hkv;
-  int64_t P = (units * ((int64_t)max_seq_len / 2 + 1) + kTargetParts - 1) / kTargetParts;
-  if (P < 256) P = 256;
-  if (P > kMaxPartition) P = kMaxPartition;
-  P = (P + 15) / 16 * 16;
-  return (int)P;
-}
 
 hipError_t launch_paged_decode_bf16(const PagedArgs& a, hipStream_t s) {
   const float c = a.scale * kLog2e;

@@ -36,7 +36,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRun = 8;        // rows of k_new / v_new per workgroup
+constexpr int kRun = kAppendRows;  // rows of k_new / v_new per workgroup
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;     // 16-byte moves in flight per thread and round
 constexpr int kQslLds = 4096;  // query_start_loc entries staged in LDS, at most
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       const int t0 = a.qsl != nullptr ? (staged ? qsl_s[n] : a.qsl[n]) : n;
       const int t1 = a.qsl != nullptr ? (staged ? qsl_s[n + 1] : a.qsl[n + 1]) : n + 1;
       const int pos = a.seq_lens[n] - (t1 - t0) + (t - t0);
-      const int64_t blk = a.block_table[(int64_t)n * a.max_blocks_per_seq + (pos >> 4)];
-      row_base[tid] = (blk * a.Hkv * kBlockSize + (pos & 15)) * D;
+      const int32_t entry = a.block_table[(int64_t)n * a.max_blocks_per_seq + (pos >> 4)];
+      row_base[tid] = paged_kv_offset(entry, 0, a.Hkv, D) + (pos & 15) * D;
     }
   }
   __syncthreads();
@@ -126,8 +126,6 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 }
 
 }  // namespace
-
-int append_grid(int num_tokens) { return (num_tokens + kRun - 1) / kRun; }
 
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)append_grid(a.num_tokens));

@@ -232,7 +232,7 @@ __device__ __forceinline__ void pp_copy(const char* base, const KvSrc<PAGED>& sr
       }
     } else {
       const int key = min(n0 + t, kv_len - 1);
-      const int64_t row = (int64_t)src.table[key >> 4] * src.block_bytes + (key & 15) * C::ROW;
+      const int64_t row = paged_block_index(src.table[key >> 4]) * src.block_bytes + (key & 15) * C::ROW;
       copy_vaddr(base + row + (off[s] - (uint32_t)(t * C::ROW)), l);
     }
   }
@@ -261,7 +261,7 @@ __device__ __forceinline__ void pp_copy_paged(const char* base, int64_t block_by
 #pragma unroll
   for (int s = 0; s < C::CP; ++s) {
     const int tb = (wave * C::CP + s) * C::RPC;  // first tile row of copy s
-    const char* row = base + (int64_t)blk[s] * block_bytes + ((n0 + tb) & 15) * C::ROW;
+    const char* row = base + paged_block_index(blk[s]) * block_bytes + ((n0 + tb) & 15) * C::ROW;
     copy_saddr(row, off[s] - (uint32_t)(tb * C::ROW), dst + s * 1024);
   }
 }
