@@ -165,6 +165,131 @@ def decode_parity(bd):
     return float(err.max()), float(err.mean())
 
 
+def machine_info(dev):
+    """GPU name and compute units as the runtime reports them; XCDs derived
+    from the compute units."""
+    pr = torch.cuda.get_device_properties(dev)
+    info = {"gpu": pr.name, "arch": getattr(pr, "gcnArchName", ""),
+            "compute_units": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2**30, 1)}
+    # 32 compute units per XCD on MI355X
+    info["xcds"] = max(1, pr.multi_processor_count // 32)
+    return info
+
+
+def probe_clock(dev, iters=20000):
+    """Shader clock under dense bf16 MFMA load, from s_memtime / s_memrealtime
+    (constant 100 MHz) of a pure MFMA loop on every SIMD, and the MFMA rate
+    that loop reaches (libattn_probe.so; not the attention library)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_tiled_amd", "libattn_probe.so"))
+    lib.attn_probe_mfma_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros(3 * blocks * 4, dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = None
+    for _ in range(2):  # the first run warms the clock up
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if lib.attn_probe_mfma_clock(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) != 0:
+            return None
+        e1.record()
+        torch.cuda.synchronize()
+        res = out.view(-1, 3).cpu().numpy()
+        ms = e0.elapsed_time(e1)
+    dt, dr = res[:, 0].astype(np.float64), res[:, 1].astype(np.float64)
+    clock_ghz = float(dt.sum() / dr.sum() * 0.1)      # s_memrealtime counts at 100 MHz
+    loop_s = float(dr.max()) / 1e8
+    flops = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    return {"mfma_loaded_clock_ghz": round(clock_ghz, 3),
+            "mfma_loop_tflops": round(flops / loop_s / 1e12, 1),
+            "mfma_loop_frac_of_2516": round(flops / loop_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "probe_ms_events": round(ms, 3), "probe_ms_realtime": round(loop_s * 1e3, 3)}
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
+    """Read + write GB/s of a plain device-to-device copy of nbytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t = Timer()
+    for _ in range(reps):
+        e = t.start()
+        dst.copy_(src)
+        t.stop(e)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def measure_c2(dev, steps=50, warmup=10):
+    """Causal prefill bf16, B=4, Hq=Hkv=16, T=2048, d=128 alone."""
+    cfg = (4, 16, 16, 2048, 128, torch.bfloat16, 2)
+    p = make_prefill(cfg, dev)
+    for _ in range(warmup):
+        run_prefill(p)
+    torch.cuda.synchronize()
+    t = Timer()
+    for _ in range(steps):
+        e = t.start()
+        run_prefill(p)
+        t.stop(e)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    tf = causal_flops(4, 16, 2048, 128) / (ms * 1e-3) / 1e12
+    return {"workload": "causal prefill bf16 B=4 Hq=Hkv=16 T=2048 d=128", "ms": round(ms, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+
+
+def measure_mixed(dev, ctx, steps=20, warmup=5):
+    """The mixed paged batch: 8 chunks of 512 new tokens + 256 decodes with
+    lengths uniform in [1024, 32768], Hq=32, Hkv=8, d=128, one attn_decode_paged
+    call. ctx: each chunk also follows L - 512 cached tokens (L uniform in
+    [1024, 32768]). Reported against the sum of the chunks' MFMA time and the
+    K/V bytes' HBM time at peak (the step bound)."""
+    n_chunks, n_dec = 8, 256
+    b = inputs.mixed_batch_inputs(n_chunks, 512, n_dec, (1024, 32768), 32, 8, 128,
+                                  seed=7 if ctx else 5, device=dev,
+                                  chunk_len_range=(1024, 32768) if ctx else None)
+    dec_lens = b["seq_lens_host"][n_chunks:]
+    chunk_lens = b["seq_lens_host"][:n_chunks]
+    b["o"] = torch.empty_like(b["q"])
+    b["ws"] = torch.empty(attn.decode_paged_workspace_size(
+        n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        run_decode(b, with_qsl=True)
+    torch.cuda.synchronize()
+    t = Timer()
+    for _ in range(steps):
+        e = t.start()
+        run_decode(b, with_qsl=True)
+        t.stop(e)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    fl = sum(4.0 * 32 * 128 * (512 * (L - 512) + 512 * 513 / 2) for L in chunk_lens)
+    kv = (sum(dec_lens) + sum(chunk_lens)) * 8 * 128 * 2 * 2
+    qo = (n_chunks * 512 + n_dec) * 32 * 128 * 2 * 2
+    bound_s = fl / (PEAK_BF16_TFLOPS * 1e12) + (kv + qo) / (PEAK_HBM_GBS * 1e9)
+    del b
+    torch.cuda.empty_cache()
+    name = ("mixed paged batch bf16: 8 chunks x 512 new tokens" +
+            (" after 512..32256 cached tokens" if ctx else "") +
+            " + 256 decodes L~U[1024,32768], Hq=32 Hkv=8 d=128")
+    return {"workload": name, "ms": round(ms, 4), "chunk_gflop": round(fl / 1e9, 2),
+            "kv_gbytes": round(kv / 1e9, 3),
+            "kv_gbs_whole_call": round(kv / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "mfma+hbm", "achieved": round(bound_s * 1e3, 4),
+                         "peak": round(ms, 4), "unit": "ms (step bound at peak / measured)",
+                         "frac": round(bound_s * 1e3 / ms, 4), "traffic": None}}
+
+
 def headline(args, dev):
     P_CFG = (1, 32, 8, 16384, 128, torch.bfloat16, 3)
     D_CFG = dict(num_seqs=64, Hq=12, Hkv=2, d=128, lo=256, hi=4096, seed=4)
@@ -205,6 +330,19 @@ def headline(args, dev):
     heads = tuple(range(0, 32, 2))  # 16 of the 32 query heads, every KV group
     cpu_tflops, cpu_s, pmax, pmean = cpu_baseline_prefill(p, heads=heads)
 
+    # outside the timed region: the run's machine, its clock under MFMA load,
+    # a plain copy's bandwidth, and the other configurations of the workload
+    part = attn.decode_paged_partition_size(64, 2, max(bd["max_seq_len"] for bd in dsets))
+    del dsets
+    torch.cuda.empty_cache()
+    meta = machine_info(dev)
+    meta["copy_gbs_read_plus_write"] = copy_bandwidth(dev)
+    clk = probe_clock(dev)
+    if clk is not None:
+        meta.update(clk)
+    extra = {"c2": measure_c2(dev), "c5": measure_mixed(dev, ctx=False),
+             "c5ctx": measure_mixed(dev, ctx=True)}
+
     return {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -225,8 +363,7 @@ def headline(args, dev):
             "prefill": {"B": 1, "Hq": 32, "Hkv": 8, "T": 16384, "d": 128, "causal": True},
             "decode": {"num_seqs": 64, "Hq": 12, "Hkv": 2, "d": 128, "block_size": 16,
                        "seq_len_range": [256, 4096],
-                       "partition_size": attn.decode_paged_partition_size(64, 2, max(
-                           bd["max_seq_len"] for bd in dsets))},
+                       "partition_size": part},
         },
         "prefill": {"ms": round(ms_p, 4), "tflops": round(tflops, 2),
                     "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -242,6 +379,8 @@ def headline(args, dev):
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": measured_traffic(
                                 "decode_kernel<128> 64 seqs Hq=12 Hkv=2 (mean of 8 rotated pools)")},
+        "machine": meta,
+        "other_configs": extra,
         "cpu_baseline": {"value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads(),
                          "kind": "oracle",
                          "sample": f"fp64 numpy oracle on the even query heads of the prefill "

@@ -22,6 +22,9 @@ ARCH = "gfx950"
 SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
            "decode_noalloc.hip",
            "kv_append.hip", "add_rmsnorm.hip"]
+# the benchmark's measurement probe: a library of its own, not part of libattn
+PROBE_SOURCES = ["probe.hip"]
+PROBE_OUT = os.path.join(PKG, "libattn_probe.so")
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -47,20 +50,27 @@ def _compile(src, extra):
     return obj, errs
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose=False, extra_flags=()):
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
     if verbose:
         for _, errs in results:
             if errs.strip():
                 print(errs, file=sys.stderr)
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    objs = [o for o, _ in results]
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     return OUT
 
 
