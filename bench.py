@@ -261,8 +261,9 @@ def measure_mixed(dev, ctx, steps=20, warmup=5):
     dec_lens = b["seq_lens_host"][n_chunks:]
     chunk_lens = b["seq_lens_host"][:n_chunks]
     b["o"] = torch.empty_like(b["q"])
-    b["ws"] = torch.empty(attn.decode_paged_workspace_size(
-        n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8, device=dev)
+    b["ws"] = torch.empty(attn.paged_workspace_size(
+        n_chunks + n_dec, b["q"].shape[0], 32, 8, 128, b["max_seq_len"], b["max_query_len"],
+        PARTITION), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         run_decode(b, with_qsl=True)
     torch.cuda.synchronize()
@@ -445,9 +446,9 @@ def single(args, dev):
         dec_lens = b["seq_lens_host"][n_chunks:]
         chunk_lens = b["seq_lens_host"][:n_chunks]
         b["o"] = torch.empty_like(b["q"])
-        b["ws"] = torch.empty(attn.decode_paged_workspace_size(
-            n_chunks + n_dec, 32, 8, 128, b["max_seq_len"], PARTITION), dtype=torch.uint8,
-            device=dev)
+        b["ws"] = torch.empty(attn.paged_workspace_size(
+            n_chunks + n_dec, b["q"].shape[0], 32, 8, 128, b["max_seq_len"], b["max_query_len"],
+            PARTITION), dtype=torch.uint8, device=dev)
         for _ in range(args.warmup):
             run_decode(b, with_qsl=True)
         torch.cuda.synchronize()

@@ -116,6 +116,24 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
                                         int max_seq_len, int partition_size);
 
 /*
+ * attn_paged_workspace_size — bytes of device workspace that
+ * attn_decode_paged (and attn_decode_paged_noalloc, from its fixed array)
+ * needs for a batch that may hold sequences with several query tokens:
+ * num_tokens and max_query_len as passed to attn_decode_paged. Besides the
+ * split-KV partials it holds, for batches of up to 2048 sequences with
+ * max_query_len >= 2, the work plan of the chunk rows (a few bytes per chunk
+ * query tile and KV head) and, when max_seq_len > 4096, the partial results
+ * of their key pieces: where the chunk rows alone would leave compute units
+ * idle, a chunk row's keys are split into pieces of at least 4096 keys,
+ * processed in parallel and merged by log-sum-exp, so that one long row does
+ * not hold a compute unit alone. With max_query_len == 1 it equals
+ * attn_decode_paged_workspace_size. Returns 0 if the arguments are out of
+ * range. Same contents rules as above.
+ */
+size_t attn_paged_workspace_size(int num_seqs, int num_tokens, int Hq, int Hkv, int d,
+                                 int max_seq_len, int max_query_len, int partition_size);
+
+/*
  * attn_decode_paged — attention of the batch's query tokens against a paged
  * KV cache.
  *
@@ -136,16 +154,20 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
  *                  query per sequence (row n) that sees all L_n keys.
  *   lse          : [num_tokens][Hq] fp32, optional (NULL = not written).
  *   workspace    : device memory of at least
- *                  attn_decode_paged_workspace_size(...) bytes, 256-byte
- *                  aligned.
+ *                  attn_paged_workspace_size(num_seqs, num_tokens, Hq, Hkv,
+ *                  d, max_seq_len, max_query_len, partition_size) bytes
+ *                  (which is attn_decode_paged_workspace_size(...) when
+ *                  max_query_len == 1), 256-byte aligned.
  * Host-side bounds (the caller knows them; nothing is read back):
  *   max_seq_len   >= every L_n;  max_query_len >= every q_len_n (1 when
  *   query_start_loc is NULL);  max_blocks_per_seq >= ceil(max_seq_len/16).
  * Sequences with q_len_n == 1 take the split-KV decode path (partitions of
  * partition_size tokens, 0 = automatic, else a positive multiple of 16, then
  * a log-sum-exp merge); sequences with q_len_n >= 2 take the tiled prefill
- * path reading K/V tiles through the block table. partition_size is at most
- * 4096 (larger: ATTN_ERR_UNSUPPORTED).
+ * path reading K/V tiles through the block table; when the batch has at
+ * most 2048 sequences, a 256-row query tile's keys may be split into pieces
+ * of at least 4096 keys merged by log-sum-exp (see attn_paged_workspace_size).
+ * partition_size is at most 4096 (larger: ATTN_ERR_UNSUPPORTED).
  * Preconditions not checked on the device: table entries for logical blocks
  * < ceil(L_n/16) lie in [0, num_blocks); 0 <= L_n <= max_seq_len;
  * q_len_n <= L_n; query_start_loc is non-decreasing with qsl[num_seqs] <=
@@ -155,7 +177,7 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d,
  * Supported: d in {64, 128}; dtype ATTN_BF16; block_size == 16;
  * Hq % Hkv == 0 and Hq / Hkv <= 16.
  * What the call writes (o, lse, the first
- * attn_decode_paged_workspace_size(...) bytes of workspace) must not overlap
+ * attn_paged_workspace_size(...) bytes of workspace) must not overlap
  * any input (q, the caches, block_table, seq_lens, query_start_loc) or
  * another output: ATTN_ERR_SHAPE.
  * Returns ATTN_OK or a negative status; on error nothing is launched.
@@ -179,7 +201,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * layouts, results and errors are those of attn_decode_paged (same kernels,
  * bitwise the same output for the same partition size), plus:
  *   - ATTN_ERR_SCRATCH when the request needs more than the fixed array
- *     (attn_decode_paged_workspace_size(...) > ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+ *     (attn_paged_workspace_size(...) > ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
  *     nothing is launched then.
  *   - ATTN_ERR_LAUNCH if the array's device address cannot be obtained.
  * Every call on one GPU shares that GPU's array: calls that overlap in time

@@ -89,13 +89,22 @@ static void check_decode() {
   const size_t o_bytes = ((size_t)64 * 12 * p.max_parts * 128 * 4 + 255) / 256 * 256;
   CHECK((uintptr_t)p.ws_lse == W + o_bytes);
   CHECK(o_bytes + ((size_t)64 * 12 * p.max_parts * 4 + 255) / 256 * 256 == need);
-  // good: a mixed batch with chunks takes the chunk launcher too
-  const size_t need2 = attn_decode_paged_workspace_size(8, 8, 2, 128, 700, 32);
+  // good: a mixed batch with chunks takes the chunk launcher too, with its
+  // work plan after the decode partials (no key pieces: 700 keys fit one)
+  const size_t dec2 = attn_decode_paged_workspace_size(8, 8, 2, 128, 700, 32);
+  const size_t need2 = attn_paged_workspace_size(8, 500, 8, 2, 128, 700, 300, 32);
+  const int64_t cap2 = attn::plan_head_groups(8, 500, 8, 2, false);
+  CHECK(cap2 == 2 * (8 + 2));
+  CHECK(need2 == dec2 + (16 + 16 * cap2 + 255) / 256 * 256);
+  CHECK(decode(A(W), dec2, 8, 500, 8, 2, 700, 300, (const int32_t*)A(QSL), 32) ==
+        ATTN_ERR_WORKSPACE);
   CHECK(decode(A(W), need2, 8, 500, 8, 2, 700, 300, (const int32_t*)A(QSL), 32) == ATTN_OK);
   CHECK(g_stub.paged_prefill == before.paged_prefill + 1 &&
         g_stub.paged_decode == before.paged_decode + 2);
   CHECK(g_stub.paged.qsl == A(QSL) && g_stub.paged.max_query_len == 300 &&
         g_stub.paged.partition_size == 32);
+  CHECK((uintptr_t)g_stub.paged.chunk_plan == W + dec2 && g_stub.paged.plan_cap == cap2);
+  CHECK(g_stub.paged.chunk_pieces == 1 && g_stub.paged.chunk_o == nullptr);
 }
 
 static void check_noalloc() {

@@ -224,3 +224,35 @@ def test_noalloc_limit_matches_header(lib):
     assert "ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
     assert attn.DECODE_NOALLOC_SCRATCH_BYTES == 64 << 20
     assert attn.status_string(SCRATCH) != "unknown status"
+
+
+def test_paged_workspace_size_adds_chunk_plan_and_pieces(lib):
+    dec = attn.decode_paged_workspace_size(264, 32, 8, 128, 32768, 0)
+    # one query per sequence: the same as the decode-only size
+    assert attn.paged_workspace_size(264, 264, 32, 8, 128, 32768, 1, 0) == dec
+
+    def plan(num_seqs, num_tokens, Hq, Hkv, split):
+        # head groups: Hkv per chunk query tile (at most min(num_seqs,
+        # num_tokens / 2) + ceil(num_tokens / 256) of them) and per extra key
+        # piece (at most ceil(2 * 256 / Hq) per KV head); 16 bytes each after
+        # a 16-byte header, rounded up to 256 bytes
+        cap = Hkv * (min(num_seqs, num_tokens // 2) + -(-num_tokens // 256)
+                     + (-(-512 // Hq) if split else 0))
+        return -(-(16 + 16 * cap) // 256) * 256
+
+    # chunk rows and keys beyond one 4096-key piece: the plan, then room for
+    # the pieces' fp32 partial outputs and lse, [num_tokens][Hq][pieces][d + 1]
+    full = attn.paged_workspace_size(264, 4352, 32, 8, 128, 32768, 512, 0)
+    pieces = 32768 // 4096
+    rows = 4352 * 32 * pieces
+    assert full == dec + plan(264, 4352, 32, 8, True) + -(-rows * 128 * 4 // 256) * 256 + \
+        -(-rows * 4 // 256) * 256
+    # keys within one piece: the plan only
+    assert attn.paged_workspace_size(264, 4352, 32, 8, 128, 4096, 512, 0) == \
+        attn.decode_paged_workspace_size(264, 32, 8, 128, 4096, 0) + plan(264, 4352, 32, 8, False)
+    # a batch beyond 2048 sequences: nothing extra (one workgroup per possible
+    # chunk query tile and head, no plan and no split)
+    assert attn.paged_workspace_size(2049, 4352, 32, 8, 128, 32768, 512, 0) == \
+        attn.decode_paged_workspace_size(2049, 32, 8, 128, 32768, 0)
+    assert attn.paged_workspace_size(264, 0, 32, 8, 128, 32768, 512, 0) == 0
+    assert attn.paged_workspace_size(264, 4352, 12, 5, 128, 32768, 512, 0) == 0  # Hq % Hkv

@@ -152,6 +152,54 @@ def test_mixed_many_chunk_sequences_persistent_unsorted(d, Hq, Hkv):
     assert_lse_close(lse[rows.to(DEV)], rl, rb, "200 chunk sequences")
 
 
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 1), (128, 16, 1), (64, 8, 8)])
+def test_chunk_rows_split_along_the_keys(d, Hq, Hkv):
+    # chunk rows whose keys span more than one 4096-key piece (each query
+    # tile's key range is split evenly, the pieces run in parallel and are
+    # merged by log-sum-exp): 9000 keys (3 pieces), 5000 (2), 4200 with 200
+    # new rows (their two query tiles, of 65 and 66 key tiles, split in 2),
+    # next to decodes and a short chunk that is not split
+    seq_lens = [9000, 300, 5000, 4200, 6000, 700]
+    q_lens = [300, 1, 64, 200, 1, 129]
+    print(f"[mixed] chunk rows split along the keys d={d} Hq={Hq} Hkv={Hkv}", flush=True)
+    b = inputs.paged_inputs(len(seq_lens), Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens,
+                            seed=79 + d)
+    assert attn.paged_workspace_size(len(seq_lens), sum(q_lens), Hq, Hkv, d, max(seq_lens),
+                                     max(q_lens)) > \
+        attn.decode_paged_workspace_size(len(seq_lens), Hq, Hkv, d, max(seq_lens))
+    o, lse = run(b)
+    ro, rl, rb = ref_decode(b["q"], b["k_cache"], b["v_cache"], b["block_table"], b["seq_lens"],
+                            1.0 / math.sqrt(d), query_start_loc=b["query_start_loc"])
+    assert_close(o, ro, torch.bfloat16, "split chunk rows")
+    assert_lse_close(lse, rl, rb, "split chunk rows")
+
+
+def test_split_chunk_rows_match_unsplit_batch():
+    # the same chunk computed in a batch of more than 2048 sequences (whose
+    # chunk rows are not split) and in a small batch (split): equal within
+    # the rounding of the merge (each piece rounds its weights to bf16
+    # against its own max; bound derived as for the split-KV decode)
+    L, q_len, Hq, Hkv, d = 8200, 100, 4, 2, 128
+    small = inputs.paged_inputs(1, Hq, Hkv, d, seq_lens=[L], q_lens=[q_len], seed=81)
+    o_split, _ = run(small)
+    n = 2049
+    big_lens = [L] + [1] * (n - 1)
+    big_q = [q_len] + [1] * (n - 1)
+    big = inputs.paged_inputs(n, Hq, Hkv, d, seq_lens=big_lens, q_lens=big_q, seed=82)
+    # put the small batch's sequence into the big pool: same K/V, same q
+    t = big["block_table"][0, :-(-L // 16)].long()
+    big["k_cache"][t] = small["k_cache"][small["block_table"][0, :-(-L // 16)].long()]
+    big["v_cache"][t] = small["v_cache"][small["block_table"][0, :-(-L // 16)].long()]
+    big["q"][:q_len] = small["q"]
+    o_whole, _ = run(big)
+    a_ = o_split.float().cpu().double().numpy()
+    c_ = o_whole[:q_len].float().cpu().double().numpy()
+    V = oracle.gather_paged_kv(small["v_cache"], small["block_table"][0].numpy(), L)
+    vmax = np.repeat(np.abs(V).max(axis=0), Hq // Hkv, axis=0)[None]  # [1, Hq, d]
+    bound = (2.0 ** -8) * (np.abs(a_) + np.abs(c_)) * (1 + 2.0 ** -7) + (2.0 ** -7 + 2.0 ** -12) * vmax
+    assert (np.abs(a_ - c_) <= bound).all()
+
+
 def test_config_mixed_batch_full_size_sampled():
     # 8 chunks of 512 new tokens + 256 decodes with lengths uniform in
     # [1024, 32768], Hq=32, Hkv=8, d=128, one shuffled pool (~17.9 GB) drawn

@@ -68,6 +68,18 @@ def test_noalloc_matches_workspace_entry_point_twice():
     check(small, True, "mixed batch after the large one", partition_size=32)
 
 
+def test_noalloc_split_chunk_rows():
+    # chunk rows whose keys are split into pieces (9000 and 5000 keys) next to
+    # a decode: the chunk rows' work plan and the pieces' partial results
+    # live in the fixed array too, after the calls above left it dirty
+    seq_lens = [9000, 40, 5000]
+    q_lens = [300, 1, 64]
+    b = inputs.paged_inputs(len(seq_lens), 8, 2, 128, seq_lens=seq_lens, q_lens=q_lens, seed=72)
+    assert attn.paged_workspace_size(3, sum(q_lens), 8, 2, 128, max(seq_lens), max(q_lens)) < \
+        attn.DECODE_NOALLOC_SCRATCH_BYTES
+    check(b, True, "split chunk rows")
+
+
 def test_noalloc_rejects_requests_beyond_the_array():
     # 2000 sequences of up to 32768 tokens in 16-token partitions need far
     # more than the fixed array: rejected on the host, nothing launched

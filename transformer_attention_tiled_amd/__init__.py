@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     decode_paged_noalloc,
     DECODE_NOALLOC_SCRATCH_BYTES,
     decode_paged_workspace_size,
+    paged_workspace_size,
     decode_paged_partition_size,
     kv_append,
     add_rmsnorm,

@@ -70,6 +70,9 @@ def load_library():
     lib.attn_decode_paged_partition_size.restype = c_int
     lib.attn_decode_paged_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     lib.attn_decode_paged_workspace_size.restype = c_size_t
+    lib.attn_paged_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                              c_int]
+    lib.attn_paged_workspace_size.restype = c_size_t
     lib.attn_decode_paged.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p,
                                       c_int, c_int, c_int, c_int, c_int,
@@ -200,6 +203,15 @@ def decode_paged_workspace_size(num_seqs, Hq, Hkv, d, max_seq_len, partition_siz
                                                                partition_size))
 
 
+def paged_workspace_size(num_seqs, num_tokens, Hq, Hkv, d, max_seq_len, max_query_len=1,
+                         partition_size=0):
+    """attn_paged_workspace_size: workspace bytes for a batch that may hold
+    chunk rows (several query tokens per sequence)."""
+    return int(load_library().attn_paged_workspace_size(num_seqs, num_tokens, Hq, Hkv, d,
+                                                        max_seq_len, max_query_len,
+                                                        partition_size))
+
+
 def _paged_common(A, q, k_cache, v_cache, block_table, seq_lens, query_start_loc):
     A.tensor("q", q, ndim=3)
     num_tokens, Hq, d = q.shape
@@ -241,7 +253,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, max
         o = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    ws_bytes = decode_paged_workspace_size(num_seqs, Hq, Hkv, d, max_seq_len, partition_size)
+    ws_bytes = paged_workspace_size(num_seqs, num_tokens, Hq, Hkv, d, max_seq_len,
+                                    max_query_len, partition_size)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -49,18 +49,28 @@ bool policy_in_range(int num_seqs, int Hkv, int max_seq_len) {
   return mul({num_seqs, Hkv, (int64_t)max_seq_len / 2 + 1, 2}, &est);
 }
 
-// Bytes of the split-KV workspace: partial outputs, then partial lse.
+// Bytes of the paged-call workspace: the decode partitions' partial outputs
+// and lse, then for batches with chunk rows (q_len >= 2) of up to
+// kPagedMaxSeqs sequences the chunk rows' work plan and (when their keys may
+// span several pieces) the pieces' partial outputs and lse.
 struct WsLayout {
   int partition_size = 0;
   int max_parts = 0;
   size_t o_bytes = 0;
   size_t l_bytes = 0;
+  int plan_cap = 0;
+  size_t plan_bytes = 0;
+  int chunk_pieces = 1;
+  size_t co_bytes = 0;
+  size_t cl_bytes = 0;
   size_t total = 0;
 };
 
-bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partition_size,
-               WsLayout* w) {
-  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || max_seq_len < 1 || !supported_d(d)) return false;
+bool ws_layout(int num_seqs, int num_tokens, int Hq, int Hkv, int d, int max_seq_len,
+               int max_query_len, int partition_size, WsLayout* w) {
+  if (num_seqs < 1 || num_tokens < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 1 ||
+      max_query_len < 1 || !supported_d(d))
+    return false;
   if (partition_size < 0 || partition_size % attn::kBlockSize != 0 ||
       partition_size > attn::kMaxPartition)
     return false;
@@ -74,11 +84,35 @@ bool ws_layout(int num_seqs, int Hq, int Hkv, int d, int max_seq_len, int partit
     return false;
   const int64_t o_bytes = (ob + 255) / 256 * 256;
   const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  int64_t co_bytes = 0, cl_bytes = 0, plan_bytes = 0, cap = 0;
+  int pieces = 1;
+  if (max_query_len >= 2 && num_seqs <= attn::kPagedMaxSeqs) {
+    const int64_t piece_keys = 64LL * attn::kChunkPieceTiles;
+    const int64_t np = ((int64_t)max_seq_len + piece_keys - 1) / piece_keys;
+    if (np >= 2) {
+      int64_t crows, cob;
+      if (!mul({num_tokens, Hq, np}, &crows) || !mul({crows, d, 4}, &cob) ||
+          cob > (INT64_MAX >> 3))
+        return false;
+      co_bytes = (cob + 255) / 256 * 256;
+      cl_bytes = (crows * 4 + 255) / 256 * 256;
+      pieces = (int)np;
+    }
+    cap = attn::plan_head_groups(num_seqs, num_tokens, Hq, Hkv, pieces > 1);
+    // the planned grid has ceil(cap / 8) * 8 * (Hq / Hkv) workgroups
+    if (cap > INT32_MAX / 8 || (cap + 7) / 8 * 8 * (Hq / Hkv) > INT32_MAX) return false;
+    plan_bytes = (16 + 16 * cap + 255) / 256 * 256;
+  }
   w->partition_size = P;
   w->max_parts = (int)parts;
   w->o_bytes = (size_t)o_bytes;
   w->l_bytes = (size_t)l_bytes;
-  w->total = (size_t)(o_bytes + l_bytes);
+  w->plan_cap = (int)cap;
+  w->plan_bytes = (size_t)plan_bytes;
+  w->chunk_pieces = pieces;
+  w->co_bytes = (size_t)co_bytes;
+  w->cl_bytes = (size_t)cl_bytes;
+  w->total = (size_t)(o_bytes + l_bytes + plan_bytes + co_bytes + cl_bytes);
   return true;
 }
 
@@ -156,7 +190,9 @@ int decode_paged_run(const DecodeRequest& r, void* workspace, size_t workspace_b
       !aligned(lse, 4) || !aligned(workspace, 256))
     return ATTN_ERR_ALIGN;
   WsLayout w;
-  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return ATTN_ERR_SHAPE;
+  if (!ws_layout(num_seqs, num_tokens, Hq, Hkv, d, max_seq_len, max_query_len, partition_size,
+                 &w))
+    return ATTN_ERR_SHAPE;
   if (scratch == nullptr && (workspace == nullptr || workspace_bytes < w.total))
     return ATTN_ERR_WORKSPACE;
   if (scratch != nullptr && w.total > kNoAllocScratchBytes) return ATTN_ERR_SCRATCH;
@@ -199,8 +235,16 @@ int decode_paged_run(const DecodeRequest& r, void* workspace, size_t workspace_b
   a.max_blocks_per_seq = max_blocks_per_seq; a.max_seq_len = max_seq_len;
   a.max_query_len = max_query_len; a.num_blocks = num_blocks; a.scale = r.scale;
   a.partition_size = w.partition_size; a.max_parts = w.max_parts;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_bytes);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_lse = reinterpret_cast<float*>(ws + w.o_bytes);
+  char* chunk = ws + w.o_bytes + w.l_bytes;
+  a.chunk_plan = w.plan_cap > 0 ? reinterpret_cast<int*>(chunk) : nullptr;
+  a.plan_cap = w.plan_cap;
+  a.chunk_pieces = w.chunk_pieces;
+  a.chunk_o = w.chunk_pieces > 1 ? reinterpret_cast<float*>(chunk + w.plan_bytes) : nullptr;
+  a.chunk_lse =
+      w.chunk_pieces > 1 ? reinterpret_cast<float*>(chunk + w.plan_bytes + w.co_bytes) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_query_len >= 2) {
     if (launch_paged_prefill_bf16(a, s) != hipSuccess) return ATTN_ERR_LAUNCH;
@@ -272,7 +316,16 @@ int attn_decode_paged_partition_size(int num_seqs, int Hkv, int max_seq_len) {
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int Hkv, int d, int max_seq_len,
                                         int partition_size) {
   WsLayout w;
-  if (!ws_layout(num_seqs, Hq, Hkv, d, max_seq_len, partition_size, &w)) return 0;
+  if (!ws_layout(num_seqs, num_seqs, Hq, Hkv, d, max_seq_len, 1, partition_size, &w)) return 0;
+  return w.total;
+}
+
+size_t attn_paged_workspace_size(int num_seqs, int num_tokens, int Hq, int Hkv, int d,
+                                 int max_seq_len, int max_query_len, int partition_size) {
+  WsLayout w;
+  if (!ws_layout(num_seqs, num_tokens, Hq, Hkv, d, max_seq_len, max_query_len, partition_size,
+                 &w))
+    return 0;
   return w.total;
 }
 

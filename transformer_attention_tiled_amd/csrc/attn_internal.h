@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/attn.h"
 #include "paged_index.h"
 
@@ -41,7 +43,41 @@ struct PagedArgs {
   int max_parts;       // ceil(max_seq_len / partition_size)
   float* ws_o;         // split-KV partial outputs [num_seqs][Hq][max_parts][d]
   float* ws_lse;       // split-KV partial log2-sum-exp [num_seqs][Hq][max_parts]
+  // chunk rows (q_len >= 2) split along the keys into pieces of at least
+  // kChunkPieceTiles key tiles: at most chunk_pieces per query tile (1: not
+  // split; then chunk_o / chunk_lse are unused)
+  int chunk_pieces;
+  float* chunk_o;      // piece partial outputs [num_tokens][Hq][chunk_pieces][d]
+  float* chunk_lse;    // piece partial log2-sum-exp [num_tokens][Hq][chunk_pieces]
+  // the chunk rows' work plan (batches of up to kPagedMaxSeqs sequences, else
+  // nullptr): [0] head groups listed, [1] key tiles per piece, from int 4 on
+  // one int4 {sequence, piece, query tile, KV head} per head group
+  int* chunk_plan;
+  int plan_cap;        // head groups the plan has room for
 };
+
+// Chunk rows are split along the keys in pieces of at least this many 64-key
+// tiles (4096 keys), by the persistent chunk kernel (batches of up to
+// kPagedMaxSeqs sequences); the workspace holds ceil(max_seq_len / 4096)
+// pieces per row.
+constexpr int kChunkPieceTiles = 64;
+constexpr int kPagedMaxSeqs = 2048;
+// The piece length spreads the chunk work over this many workgroups' worth of
+// units (one per compute unit of the chip); the plan's length bound uses it.
+constexpr int kPlanWGs = 256;
+
+// Head groups (G = Hq / Hkv units sharing keys) the plan of a paged call can
+// list: Hkv per (chunk query tile, piece). A chunk sequence has at least 2 of
+// the num_tokens query rows and at most ceil(q_len / 256) <= q_len / 256 + 1
+// query tiles; the pieces add at most 2 * kPlanWGs / Hq per KV head (the
+// piece length is at least the chunk key tiles times Hq over 2 * kPlanWGs,
+// and an item of t tiles has at most t / length + 1 pieces).
+inline int64_t plan_head_groups(int64_t num_seqs, int64_t num_tokens, int Hq, int Hkv,
+                                bool split) {
+  const int64_t tiles = std::min(num_seqs, num_tokens / 2) + (num_tokens + 255) / 256;
+  const int64_t extra = split ? (2 * kPlanWGs + Hq - 1) / Hq : 0;
+  return (int64_t)Hkv * (tiles + extra);
+}
 
 // Append to a paged cache: k_new,v_new [num_tokens][Hkv][d] written into
 // caches [num_blocks][Hkv][16][d] at the positions the block table gives.

@@ -82,6 +82,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -145,6 +146,16 @@ struct Problem {
   int kv_len;         // keys available
   int ctx;            // absolute position of query row 0 (query i sees keys <= ctx + i)
   int m0;             // first query row of this workgroup
+  // Key range: tiles tile0 .. tile1 - 1 of the workgroup's keys (the whole
+  // range: 0 .. INT_MAX). With part_o set, the workgroup writes, per query
+  // row, its normalised fp32 partial output and log2-sum-exp over that range
+  // (to be merged with the other ranges' partials) instead of o and lse.
+  int tile0 = 0;
+  int tile1 = 0x7fffffff;
+  float* part_o = nullptr;      // row 0's partial output [D] fp32
+  float* part_lse = nullptr;    // row 0's partial log2-sum-exp
+  int64_t part_stride = 0;      // floats between consecutive rows' partial outputs
+  int64_t part_lse_stride = 0;  // floats between consecutive rows' partial lse
 };
 
 // ---------------------------------------------------------------------------
@@ -346,11 +357,16 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
 
   const int wg_last_q = min(pb.m0 + kPPBM, pb.q_len);
   const int wg_keys = CAUSAL ? min(pb.kv_len, pb.ctx + wg_last_q) : pb.kv_len;
-  const int n = (wg_keys + BN - 1) / BN;
+  const int n_all = (wg_keys + BN - 1) / BN;
   const int w_last_q = min(wq0 + 32, pb.q_len);
   const int w_keys =
       wq0 >= pb.q_len ? 0 : (CAUSAL ? min(pb.kv_len, pb.ctx + w_last_q) : pb.kv_len);
-  const int wt = (w_keys + BN - 1) / BN;  // tiles this wave computes (<= n)
+  // this workgroup's key tiles: t0 .. t0 + n - 1 (a piece of the range, or
+  // all of it); the loop counts j = 0 .. n, tile t0 + j
+  const int t0 = min(pb.tile0, n_all);
+  const int n = min(pb.tile1, n_all) - t0;
+  // tiles this wave computes, counted from t0 (<= n)
+  const int wt = max(0, min((w_keys + BN - 1) / BN, t0 + n) - t0);
 
   // per-lane source offsets of the copies (tile-relative): K and V tiles
   // are swizzled differently
@@ -399,7 +415,7 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   // Q[wq0 + lq][16*s + 8*hf + e]); both are waited for before the first
   // phase, then K tiles 1, 2 and V tiles 0, 1 are put in flight (in the
   // order the waits in the loop assume: K1, V0, then K2, V1).
-  pp_copy<D, PAGED>(src.k, src, 0, pb.kv_len, kbuf(0), wave, lane, koff);
+  pp_copy<D, PAGED>(src.k, src, t0 * BN, pb.kv_len, kbuf(0), wave, lane, koff);
   bf16x8 qf[D / 16];
   {
     const int qrow = min(wq0 + lq, pb.q_len - 1);
@@ -409,10 +425,10 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
           bf16x8, *(const u32x4*)(pb.q + (int64_t)qrow * pb.row_stride + 16 * s + 8 * hf));
   }
   __builtin_amdgcn_s_waitcnt(0);
-  if (1 < n) pp_copy<D, PAGED>(src.k, src, BN, pb.kv_len, kbuf(1), wave, lane, koff);
-  pp_copy<D, PAGED>(src.v, src, 0, pb.kv_len, vbuf(0), wave, lane, voff);
-  if (2 < n) pp_copy<D, PAGED>(src.k, src, 2 * BN, pb.kv_len, kbuf(2), wave, lane, koff);
-  if (1 < n) pp_copy<D, PAGED>(src.v, src, BN, pb.kv_len, vbuf(1), wave, lane, voff);
+  if (1 < n) pp_copy<D, PAGED>(src.k, src, (t0 + 1) * BN, pb.kv_len, kbuf(1), wave, lane, koff);
+  pp_copy<D, PAGED>(src.v, src, t0 * BN, pb.kv_len, vbuf(0), wave, lane, voff);
+  if (2 < n) pp_copy<D, PAGED>(src.k, src, (t0 + 2) * BN, pb.kv_len, kbuf(2), wave, lane, koff);
+  if (1 < n) pp_copy<D, PAGED>(src.v, src, (t0 + 1) * BN, pb.kv_len, vbuf(1), wave, lane, voff);
   // fold the softmax scale in log2 units (c = scale * log2 e) into Q, once:
   // the score MFMA then yields c * s directly (each q * c rounded to bf16)
 #pragma unroll
@@ -466,8 +482,8 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   if constexpr (PAGED) {
 #pragma unroll
     for (int s = 0; s < C::CP; ++s) {
-      ev[s] = table_row(2, s);
-      ek[s] = table_row(3, s);
+      ev[s] = table_row(t0 + 2, s);
+      ek[s] = table_row(t0 + 3, s);
     }
   }
 
@@ -507,35 +523,35 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
     // before the previous barrier), then mask, running max, weights, sums.
     if (j + 3 < n) {
       const uint32_t buf = lds0 + (uint32_t)(((B + 3) % kBufs) * C::TILE);
-      if (j + 3 < n_full) {
+      if (t0 + j + 3 < n_full) {
         if constexpr (PAGED)
-          pp_copy_paged<D>(src.k, src.block_bytes, ek, (j + 3) * BN, buf + wdst, wave, koff);
+          pp_copy_paged<D>(src.k, src.block_bytes, ek, (t0 + j + 3) * BN, buf + wdst, wave, koff);
         else
-          pp_copy_full<D>(src.k + (int64_t)(j + 3) * C::TILE, buf + wdst, koff);
+          pp_copy_full<D>(src.k + (int64_t)(t0 + j + 3) * C::TILE, buf + wdst, koff);
       } else {
-        pp_copy<D, PAGED>(src.k, src, (j + 3) * BN, pb.kv_len, buf, wave, lane, koff);
+        pp_copy<D, PAGED>(src.k, src, (t0 + j + 3) * BN, pb.kv_len, buf, wave, lane, koff);
       }
     }
     if (j + 2 < n) {
       const uint32_t buf = lds0 + (uint32_t)((kBufs + (B + 2) % kBufs) * C::TILE);
-      if (j + 2 < n_full) {
+      if (t0 + j + 2 < n_full) {
         if constexpr (PAGED)
-          pp_copy_paged<D>(src.v, src.block_bytes, ev, (j + 2) * BN, buf + wdst, wave, voff);
+          pp_copy_paged<D>(src.v, src.block_bytes, ev, (t0 + j + 2) * BN, buf + wdst, wave, voff);
         else
-          pp_copy_full<D>(src.v + (int64_t)(j + 2) * C::TILE, buf + wdst, voff);
+          pp_copy_full<D>(src.v + (int64_t)(t0 + j + 2) * C::TILE, buf + wdst, voff);
       } else {
-        pp_copy<D, PAGED>(src.v, src, (j + 2) * BN, pb.kv_len, buf, wave, lane, voff);
+        pp_copy<D, PAGED>(src.v, src, (t0 + j + 2) * BN, pb.kv_len, buf, wave, lane, voff);
       }
     }
     if constexpr (PAGED) {
 #pragma unroll
       for (int s = 0; s < C::CP; ++s) {
         ev[s] = ek[s];
-        ek[s] = table_row(j + 4, s);
+        ek[s] = table_row(t0 + j + 4, s);
       }
     }
     if (j < wt) {
-      const int n0 = j * BN;
+      const int n0 = (t0 + j) * BN;
       const bool diag = CAUSAL ? (n0 + BN - 1 > pb.ctx + wq0) : false;
       if (diag || n0 + BN > pb.kv_len) {
         // register (kb, r) holds key n0 + 8 hf + o, o = 32 kb + 16 (r >> 3) +
@@ -620,6 +636,14 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
     }
+    if constexpr (PAGED) {
+      // the table entries read at the start of this phase are taken into
+      // registers here: a scalar load still in flight in the next M phase
+      // would make each of its LDS operand reads wait for all outstanding
+      // reads (scalar loads complete out of order), serialising the phase
+#pragma unroll
+      for (int s = 0; s < C::CP; ++s) asm volatile("" ::"s"(ek[s]));
+    }
     phase_barrier();
   };
   static_assert(kBufs == 4, "the loop below is unrolled by kBufs");
@@ -644,6 +668,26 @@ __device__ __forceinline__ void run_pp(const Problem& pb, const KvSrc<PAGED>& sr
   // the next kernel on the stream reads HBM.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (pb.part_o != nullptr) {
+    // a piece of the key range: the normalised fp32 partial of each row
+    // (lane: 4 consecutive d per register group, d = 32 db + 8 g4 + 4 hf)
+    // and its log2-sum-exp, merged later with the other pieces'
+    const int qrow = wq0 + lq;
+    if (qrow < pb.q_len) {
+      float* dst = pb.part_o + (int64_t)qrow * pb.part_stride + 4 * hf;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(f32x4*)(dst + 32 * db + 8 * g4) =
+              f32x4{acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                    acc[db][4 * g4 + 3] * inv};
+      if (hf == 0)
+        pb.part_lse[(int64_t)qrow * pb.part_lse_stride] =
+            l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+    }
+    return;
+  }
   {
     // row-major tile, 16-byte chunks XOR-swizzled by row so that the 32 rows
     // of one staging write spread over the banks
@@ -730,27 +774,79 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_kernel(PrefillArgs a,
 
 // Chunked prefill of a paged batch: the sequences with q_len >= 2 (their
 // K/V tiles gathered through the block table), with the two-group kernel.
-// Work items are (sequence, 256-row query tile, query head).
+// Work units are (sequence, 256-row query tile, query head), or a piece of
+// one's key range when long rows are split along the keys.
 //
-// PERSISTENT (batches of up to kPagedMaxSeqs sequences): the items are
-// listed over the chunk sequences only, longest sequence first and, within
-// a sequence, its last query tile (the most keys) first. Each workgroup
-// builds that list once in LDS (the chunk sequences, their order and the
-// index of each one's first item), then takes one item per round, the
-// rounds alternating direction over the workgroups, until the list ends: a
-// static longest-first assignment. A batch that mixes a few chunks with many
-// single-token decodes thus launches no workgroup without work. Consecutive
-// items (the query heads of one tile, GQA siblings first) go to workgroups
-// on one XCD, whose L2 then serves their shared K/V tiles.
-// Otherwise one workgroup per (query tile, sequence, head) of the host's
-// bound; workgroups of sequences with fewer rows exit at once.
-constexpr int kPagedMaxSeqs = 2048;
-constexpr int kSortMax = 128;  // chunk sequences ordered by length, at most
+// Planned (batches of up to kPagedMaxSeqs sequences): one workgroup plans the
+// call first. It lists the chunk sequences, orders them by the size of their
+// largest unit (up to kSortMax of them; more keep batch order), picks the
+// piece length (chunk_piece_target) and writes the list of head groups: a
+// head group is (sequence, key piece, query tile, KV head), the G = Hq / Hkv
+// units whose query heads read the same keys. Per sequence they are listed
+// piece by piece, within a piece the last query tile (the most keys) first,
+// within a tile KV head by KV head. Then one workgroup per unit, none looping
+// over units: head group j runs on XCD j mod 8 (workgroups are dealt out to
+// the XCDs round-robin) in slot j div 8, so each XCD takes every eighth head
+// group, largest first, and its L2 serves the G query heads of each one (and
+// with Hkv = 8, every query tile of a KV head). Workgroups past the list's end
+// exit at once; the host sizes the grid by a bound on its length.
+// Otherwise (more sequences) one workgroup per (query tile, sequence, head)
+// of the host's bound, no split; workgroups of sequences with fewer rows exit
+// at once.
+constexpr int kSortMax = 128;      // chunk sequences ordered by unit size, at most
+constexpr int kPlanThreads = 1024;
+constexpr int kChunkSplitFactor = 2;  // units per compute unit the split aims at
 
+// Key tiles of query tile qt of a chunk sequence (L keys, q_len queries
+// at the end, the query at position t seeing keys 0..t), as run_pp counts
+// them.
+__device__ __forceinline__ int chunk_item_tiles(int L, int q_len, int qt) {
+  const int last_q = min((qt + 1) * kPPBM, q_len);
+  return (min(L, L - q_len + last_q) + BN - 1) / BN;
+}
+
+// Key tiles per piece the call aims at: all chunk items' key tiles (over
+// every query head) spread over kChunkSplitFactor units per workgroup of a
+// nominal grid of kPlanWGs (one per compute unit), never below
+// kChunkPieceTiles. Items already short enough stay whole, so a batch whose
+// chunk rows fill the chip by themselves is barely split. Computed by one
+// wave (lanes stride the sequences).
+__device__ int chunk_piece_target(const PagedArgs& a) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0;
+  for (int n = lane; n < a.num_seqs; n += 64) {
+    const int q_len = a.qsl[n + 1] - a.qsl[n];
+    if (q_len < 2) continue;
+    const int L = a.seq_lens[n];
+    const int cnt = (q_len + kPPBM - 1) / kPPBM;
+    for (int qt = 0; qt < cnt; ++qt) tot += chunk_item_tiles(L, q_len, qt);
+  }
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) tot += __shfl_xor(tot, dd);
+  const long long per_unit = (long long)kChunkSplitFactor * kPlanWGs;
+  return (int)max((long long)kChunkPieceTiles, (tot * a.Hq + per_unit - 1) / per_unit);
+}
+
+// Pieces an item of `tiles` key tiles splits into at that target (1 when the
+// call does not split chunk items, a.chunk_pieces == 1). The target is at
+// least kChunkPieceTiles, so this stays within the chunk_pieces slots the
+// workspace holds; the min only keeps it there should seq_lens exceed the
+// max_seq_len the workspace was sized for. Piece k holds tiles
+// k * tiles / np .. (k + 1) * tiles / np - 1.
+__device__ __forceinline__ int chunk_item_pieces(const PagedArgs& a, int tiles, int target) {
+  if (a.chunk_pieces <= 1) return 1;
+  return min(a.chunk_pieces, max(1, (tiles - 1) / target + 1));
+}
+
+// One chunk item, or one piece of its key range. Returns false (uniformly,
+// having done nothing) if the item has no such piece.
 template <int D>
-__device__ __forceinline__ void run_paged_item(const PagedArgs& a, float c, char* lds, int n,
-                                               int qt, int h, int t0, int q_len) {
-  const int L = a.seq_lens[n];
+__device__ __forceinline__ bool run_paged_item(const PagedArgs& a, float c, char* lds, int n,
+                                               int qt, int h, int t0, int q_len, int L,
+                                               int piece, int target) {
+  const int tiles = chunk_item_tiles(L, q_len, qt);
+  const int np = chunk_item_pieces(a, tiles, target);
+  if (piece >= np) return false;
   const int g = h / (a.Hq / a.Hkv);
   Problem pb;
   pb.q = (const uint16_t*)a.q + ((int64_t)t0 * a.Hq + h) * D;
@@ -762,115 +858,240 @@ __device__ __forceinline__ void run_paged_item(const PagedArgs& a, float c, char
   pb.kv_len = L;
   pb.ctx = L - q_len;
   pb.m0 = qt * kPPBM;
+  if (np > 1) {
+    const int64_t slot = ((int64_t)t0 * a.Hq + h) * a.chunk_pieces + piece;
+    pb.tile0 = piece * tiles / np;
+    pb.tile1 = (piece + 1) * tiles / np;
+    pb.part_o = a.chunk_o + slot * D;
+    pb.part_lse = a.chunk_lse + slot;
+    pb.part_stride = (int64_t)a.Hq * a.chunk_pieces * D;
+    pb.part_lse_stride = (int64_t)a.Hq * a.chunk_pieces;
+  }
   KvSrc<true> src;
   src.k = (const char*)((const uint16_t*)a.k_cache + (int64_t)g * kBlockSize * D);
   src.v = (const char*)((const uint16_t*)a.v_cache + (int64_t)g * kBlockSize * D);
   src.table = a.block_table + (int64_t)n * a.max_blocks_per_seq;
   src.block_bytes = (int64_t)a.Hkv * kBlockSize * D * 2;
   run_pp<D, true, true>(pb, src, c, lds);
+  return true;
 }
 
-template <int D, bool PERSISTENT>
+template <int D>
 __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_paged_kernel(PagedArgs a, float c,
                                                                          int n_qt) {
   __shared__ __attribute__((aligned(1024))) char lds[PP<D>::LDS];
-  if constexpr (!PERSISTENT) {
-    const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    int unit, qt;
-    logical_to_work(logical, a.num_seqs * a.Hq, n_qt, unit, qt);
-    const int n = unit / a.Hq, h = unit % a.Hq;
-    const int t0 = a.qsl[n];
-    const int q_len = a.qsl[n + 1] - t0;
-    if (q_len < 2 || qt * kPPBM >= q_len) return;  // uniform over the workgroup
-    run_paged_item<D>(a, c, lds, n, qt, h, t0, q_len);
-  } else {
-    // the chunk sequences, longest first (up to kSortMax of them; more keep
-    // batch order), with the index of each one's first item
-    __shared__ int seq_of[kPagedMaxSeqs];      // r-th chunk sequence
-    __shared__ int first_of[kPagedMaxSeqs];    // its first query tile in the list
-    __shared__ int scratch[kPagedMaxSeqs];
-    __shared__ int n_chunk_seqs, n_tiles;
-    if (threadIdx.x < 64) {
-      // wave 0. Pass 1: compact the sequences with q_len >= 2, in batch order,
-      // into scratch (ids) and first_of (lengths)
-      const int lane = threadIdx.x;
-      int m = 0;
-      for (int n0 = 0; n0 < a.num_seqs; n0 += 64) {
-        const int n = n0 + lane;
-        const bool chunk = n < a.num_seqs && a.qsl[n + 1] - a.qsl[n] >= 2;
-        const unsigned long long bal = __builtin_amdgcn_ballot_w64(chunk);
-        if (chunk) {
-          const int at = m + (int)__builtin_popcountll(bal & ((1ull << lane) - 1));
-          scratch[at] = n;
-          first_of[at] = a.seq_lens[n];
-        }
-        m += (int)__builtin_popcountll(bal);
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  int unit, qt;
+  logical_to_work(logical, a.num_seqs * a.Hq, n_qt, unit, qt);
+  const int n = unit / a.Hq, h = unit % a.Hq;
+  const int t0 = a.qsl[n];
+  const int q_len = a.qsl[n + 1] - t0;
+  if (q_len < 2 || qt * kPPBM >= q_len) return;  // uniform over the workgroup
+  run_paged_item<D>(a, c, lds, n, qt, h, t0, q_len, a.seq_lens[n], 0, 0x7fffffff);
+}
+
+// The plan: a.chunk_plan[0] = head groups listed, [1] = piece target, then
+// from int 4 on one int4 {sequence, piece, query tile, KV head} per head group
+// (at most a.plan_cap of them).
+__global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(PagedArgs a) {
+  __shared__ int ids[kPagedMaxSeqs];       // chunk sequences, batch order
+  __shared__ int key[kPagedMaxSeqs];       // their sort keys
+  __shared__ int seq_of[kPagedMaxSeqs];    // r-th chunk sequence of the plan
+  __shared__ int first_of[kPagedMaxSeqs];  // its first head group
+  __shared__ int s_m, s_target, s_total;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // wave 0: the piece target, and the sequences with q_len >= 2 compacted
+    // in batch order
+    const int target = a.chunk_pieces > 1 ? chunk_piece_target(a) : 0x7fffffff;
+    const int lane = tid;
+    int m = 0;
+    for (int n0 = 0; n0 < a.num_seqs; n0 += 64) {
+      const int n = n0 + lane;
+      const bool chunk = n < a.num_seqs && a.qsl[n + 1] - a.qsl[n] >= 2;
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(chunk);
+      if (chunk) ids[m + (int)__builtin_popcountll(bal & ((1ull << lane) - 1))] = n;
+      m += (int)__builtin_popcountll(bal);
+    }
+    if (lane == 0) {
+      s_m = m;
+      s_target = target;
+    }
+  }
+  __syncthreads();
+  const int m = s_m, target = s_target;
+  // sort key: the key tiles of the sequence's largest unit (a piece of its
+  // last query tile)
+  for (int i = tid; i < m; i += kPlanThreads) {
+    const int n = ids[i];
+    const int q_len = a.qsl[n + 1] - a.qsl[n];
+    const int tl = chunk_item_tiles(a.seq_lens[n], q_len, (q_len + kPPBM - 1) / kPPBM - 1);
+    const int np = chunk_item_pieces(a, tl, target);
+    key[i] = (tl + np - 1) / np;
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += kPlanThreads) {
+    if (m <= kSortMax) {
+      // rank by counting, largest first; ties keep batch order
+      const int ki = key[i];
+      int rank = 0;
+      for (int j = 0; j < m; ++j) {
+        const int kj = key[j];
+        rank += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
       }
-      // Pass 2: order by length, longest first (rank by counting; ties keep
-      // batch order), into seq_of
-      if (m <= kSortMax) {
-        for (int i = lane; i < m; i += 64) {
-          const int Li = first_of[i];
-          int rank = 0;
-          for (int j = 0; j < m; ++j) {
-            const int Lj = first_of[j];
-            rank += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
-          }
-          seq_of[rank] = scratch[i];
-        }
-      } else {
-        for (int i = lane; i < m; i += 64) seq_of[i] = scratch[i];
+      seq_of[rank] = ids[i];
+    } else {
+      seq_of[i] = ids[i];
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // wave 0: first head group of each sequence, by a running sum over
+    // Hkv * (pieces summed over its query tiles)
+    const int lane = tid;
+    int base = 0;
+    for (int r0 = 0; r0 < m; r0 += 64) {
+      const int r = r0 + lane;
+      int cnt = 0;
+      if (r < m) {
+        const int n = seq_of[r];
+        const int q_len = a.qsl[n + 1] - a.qsl[n];
+        const int L = a.seq_lens[n];
+        const int tiles = (q_len + kPPBM - 1) / kPPBM;
+        for (int qt = 0; qt < tiles; ++qt)
+          cnt += a.Hkv * chunk_item_pieces(a, chunk_item_tiles(L, q_len, qt), target);
       }
-      // Pass 3: first item of each, in that order
-      int base = 0;
-      for (int r0 = 0; r0 < m; r0 += 64) {
-        const int r = r0 + lane;
-        int cnt = 0;
-        if (r < m) {
-          const int n = seq_of[r];
-          cnt = (a.qsl[n + 1] - a.qsl[n] + kPPBM - 1) / kPPBM;
-        }
-        int incl = cnt;
+      int incl = cnt;
 #pragma unroll
-        for (int dd = 1; dd < 64; dd <<= 1) {
-          const int up = __shfl_up(incl, dd);
-          incl += lane >= dd ? up : 0;
+      for (int dd = 1; dd < 64; dd <<= 1) {
+        const int up = __shfl_up(incl, dd);
+        incl += lane >= dd ? up : 0;
+      }
+      if (r < m) first_of[r] = base + incl - cnt;
+      base += __shfl(incl, 63);
+    }
+    // the host's bound holds the list; the min only guards against seq_lens
+    // beyond the max_seq_len the workspace was sized for
+    if (lane == 0) s_total = min(base, a.plan_cap);
+  }
+  __syncthreads();
+  const int total = s_total;
+  int4* list = reinterpret_cast<int4*>(a.chunk_plan + 4);
+  for (int j = tid; j < total; j += kPlanThreads) {
+    // the sequence holding head group j: the largest r with first_of[r] <= j
+    int lo = 0, hi = m - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first_of[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    const int n = seq_of[lo];
+    int local = j - first_of[lo];
+    const int q_len = a.qsl[n + 1] - a.qsl[n];
+    const int L = a.seq_lens[n];
+    const int cnt = (q_len + kPPBM - 1) / kPPBM;
+    // its piece: a later query tile has at least as many keys, hence pieces,
+    // so the tiles that have piece p are the last cnt - t_lo of them
+    int p = 0, t_lo = 0;
+    for (;; ++p) {
+      while (t_lo < cnt && chunk_item_pieces(a, chunk_item_tiles(L, q_len, t_lo), target) <= p)
+        ++t_lo;
+      const int here = a.Hkv * (cnt - t_lo);
+      if (local < here) break;
+      local -= here;
+    }
+    list[j] = int4{n, p, cnt - 1 - local / a.Hkv, local % a.Hkv};
+  }
+  if (tid == 0) {
+    a.chunk_plan[0] = total;
+    a.chunk_plan[1] = target;
+  }
+}
+
+// One unit of the plan per workgroup: head group j = 8 (s div G) + x, query
+// head g * G + s mod G of it, for workgroup 8 s + x (on XCD x).
+template <int D>
+__global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_planned_kernel(PagedArgs a, float c) {
+  __shared__ __attribute__((aligned(1024))) char lds[PP<D>::LDS];
+  const int G = a.Hq / a.Hkv;
+  const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+  const int j = (s / G) * 8 + x;
+  if (j >= __builtin_amdgcn_readfirstlane(a.chunk_plan[0])) return;
+  const int4 e = reinterpret_cast<const int4*>(a.chunk_plan + 4)[j];
+  const int n = __builtin_amdgcn_readfirstlane(e.x);
+  const int piece = __builtin_amdgcn_readfirstlane(e.y);
+  const int qt = __builtin_amdgcn_readfirstlane(e.z);
+  const int h = __builtin_amdgcn_readfirstlane(e.w) * G + s % G;
+  const int target = __builtin_amdgcn_readfirstlane(a.chunk_plan[1]);
+  const int t0 = __builtin_amdgcn_readfirstlane(a.qsl[n]);
+  const int q_len = __builtin_amdgcn_readfirstlane(a.qsl[n + 1]) - t0;
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[n]);
+  run_paged_item<D>(a, c, lds, n, qt, h, t0, q_len, L, piece, target);
+}
+
+// Merge of the key-range pieces of the split chunk rows: per row and query
+// head, o = sum_k 2^(lse_k - M) o_k / sum_k 2^(lse_k - M), M = max_k lse_k,
+// lse = M + log2 of that sum (in natural-log units on output). One workgroup
+// per query head of each head group of piece 0 in the plan (so per (sequence,
+// query tile, query head)), one thread per 4 consecutive d of a row;
+// workgroups of other pieces, past the list or of unsplit tiles exit at once.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeBatch = 8;  // pieces whose loads are in flight together
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PagedArgs a) {
+  const int G = a.Hq / a.Hkv;
+  const int j = blockIdx.x / G;
+  if (j >= a.chunk_plan[0]) return;
+  const int4 e = reinterpret_cast<const int4*>(a.chunk_plan + 4)[j];
+  if (e.y != 0) return;
+  const int n = e.x, qt = e.z, h = e.w * G + blockIdx.x % G;
+  const int t0 = a.qsl[n];
+  const int q_len = a.qsl[n + 1] - t0;
+  const int L = a.seq_lens[n];
+  const int np = chunk_item_pieces(a, chunk_item_tiles(L, q_len, qt), a.chunk_plan[1]);
+  if (np <= 1) return;
+  constexpr int Q4 = D / 4;
+  const int P = a.chunk_pieces;
+  const int rows = min(kPPBM, q_len - qt * kPPBM);
+  for (int e = threadIdx.x; e < rows * Q4; e += kMergeThreads) {
+    const int t = t0 + qt * kPPBM + e / Q4, d0 = 4 * (e % Q4);
+    const int64_t slot = ((int64_t)t * a.Hq + h) * P;
+    // every piece's lse and partial output, kMergeBatch pieces in flight at
+    // once; the running max rescales the sums when it grows
+    float M = kNegInf, W = 0.f;
+    f32x4 acc = f32x4{};
+    for (int k0 = 0; k0 < np; k0 += kMergeBatch) {
+      float lk[kMergeBatch];
+      f32x4 ok[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        lk[i] = k0 + i < np ? a.chunk_lse[slot + k0 + i] : kNegInf;
+        ok[i] = k0 + i < np ? *(const f32x4*)(a.chunk_o + (slot + k0 + i) * D + d0) : f32x4{};
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, lk[i]);
+      if (Mb != kNegInf) {
+        const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+        W *= r;
+        acc *= r;
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+          const float w = lk[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lk[i] - Mb);
+          W += w;
+          acc += w * ok[i];
         }
-        if (r < m) first_of[r] = base + incl - cnt;
-        base += __shfl(incl, 63);
-      }
-      if (lane == 0) {
-        n_chunk_seqs = m;
-        n_tiles = base;
+        M = Mb;
       }
     }
-    __syncthreads();
-    const int m = n_chunk_seqs;
-    const int items = n_tiles * a.Hq;
-    const int G = gridDim.x;
-    const int logical = xcd_logical(blockIdx.x, G);
-    // rounds alternate direction (0 .. G-1, then G-1 .. 0), so the workgroup
-    // that took the longest item of one round takes the shortest of the next
-    for (int k = 0;; ++k) {
-      const int item = k * G + ((k & 1) ? G - 1 - logical : logical);
-      if (item >= items) break;
-      const int idx = item / a.Hq, h = item % a.Hq;
-      // the chunk sequence holding query tile idx: the largest r with
-      // first_of[r] <= idx
-      int lo = 0, hi = m - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (first_of[mid] <= idx) lo = mid; else hi = mid - 1;
-      }
-      const int r = __builtin_amdgcn_readfirstlane(lo);
-      const int n = seq_of[r];
-      const int t0 = a.qsl[n];
-      const int q_len = a.qsl[n + 1] - t0;
-      const int cnt = (q_len + kPPBM - 1) / kPPBM;
-      // within a sequence, its last query tile (the most keys) first
-      run_paged_item<D>(a, c, lds, n, cnt - 1 - (idx - first_of[r]), h, t0, q_len);
-      __syncthreads();  // the next item refills the LDS buffers
-    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    uint16_t* dst = (uint16_t*)a.o + ((int64_t)t * a.Hq + h) * D + d0;
+    *(u32x2*)dst = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv)) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv)) << 16),
+                         (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[2] * inv)) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * inv)) << 16)};
+    if (a.lse != nullptr && d0 == 0)
+      a.lse[(int64_t)t * a.Hq + h] = W > 0.f ? (M + __log2f(W)) * kLn2 : kNegInf;
   }
 }
 
@@ -897,21 +1118,34 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_paged_prefill_bf16(const PagedArgs& a, hipStream_t s) {
   const float c = a.scale * kLog2e;
-  const int n_qt = (a.max_query_len + kPPBM - 1) / kPPBM;
-  const int64_t bound = (int64_t)n_qt * a.num_seqs * a.Hq;  // items, at most
   const dim3 block(kPPW * 64);
-  if (a.num_seqs <= kPagedMaxSeqs) {
-    const dim3 grid((unsigned)std::min<int64_t>(bound, device_cu_count()));
+  if (a.chunk_plan != nullptr) {
+    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // head groups j < plan_cap, each G workgroups, dealt 8 at a time
+    const int G = a.Hq / a.Hkv;
+    const dim3 grid((unsigned)(((int64_t)a.plan_cap + 7) / 8 * 8 * G));
     if (a.d == 128)
-      hipLaunchKernelGGL((prefill_pp_paged_kernel<128, true>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_planned_kernel<128>), grid, block, 0, s, a, c);
     else
-      hipLaunchKernelGGL((prefill_pp_paged_kernel<64, true>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_planned_kernel<64>), grid, block, 0, s, a, c);
+    if (a.chunk_pieces > 1) {
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const dim3 mgrid((unsigned)((int64_t)a.plan_cap * G));
+      if (a.d == 128)
+        hipLaunchKernelGGL((chunk_merge_kernel<128>), mgrid, dim3(kMergeThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((chunk_merge_kernel<64>), mgrid, dim3(kMergeThreads), 0, s, a);
+    }
   } else {
-    const dim3 grid((unsigned)bound);
+    const int n_qt = (a.max_query_len + kPPBM - 1) / kPPBM;
+    const dim3 grid((unsigned)((int64_t)n_qt * a.num_seqs * a.Hq));
     if (a.d == 128)
-      hipLaunchKernelGGL((prefill_pp_paged_kernel<128, false>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<128>), grid, block, 0, s, a, c, n_qt);
     else
-      hipLaunchKernelGGL((prefill_pp_paged_kernel<64, false>), grid, block, 0, s, a, c, n_qt);
+      hipLaunchKernelGGL((prefill_pp_paged_kernel<64>), grid, block, 0, s, a, c, n_qt);
   }
   return hipGetLastError();
 }
