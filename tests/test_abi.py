@@ -234,10 +234,10 @@ def test_paged_workspace_size_adds_chunk_plan_and_pieces(lib):
     def plan(num_seqs, num_tokens, Hq, Hkv, split):
         # head groups: Hkv per chunk query tile (at most min(num_seqs,
         # num_tokens / 2) + ceil(num_tokens / 256) of them) and per extra key
-        # piece (at most ceil(2 * 256 / Hq) per KV head); 16 bytes each after
-        # a 16-byte header, rounded up to 256 bytes
+        # piece (at most ceil(256 / Hq) per KV head); 16 bytes each after a
+        # 16-byte header, rounded up to 256 bytes
         cap = Hkv * (min(num_seqs, num_tokens // 2) + -(-num_tokens // 256)
-                     + (-(-512 // Hq) if split else 0))
+                     + (-(-256 // Hq) if split else 0))
         return -(-(16 + 16 * cap) // 256) * 256
 
     # chunk rows and keys beyond one 4096-key piece: the plan, then room for

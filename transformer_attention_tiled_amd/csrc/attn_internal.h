@@ -62,20 +62,20 @@ struct PagedArgs {
 // pieces per row.
 constexpr int kChunkPieceTiles = 64;
 constexpr int kPagedMaxSeqs = 2048;
-// The piece length spreads the chunk work over this many workgroups' worth of
-// units (one per compute unit of the chip); the plan's length bound uses it.
+// The piece length is the chunk work's share per compute unit of a chip of
+// this many; the plan's length bound uses it.
 constexpr int kPlanWGs = 256;
 
 // Head groups (G = Hq / Hkv units sharing keys) the plan of a paged call can
 // list: Hkv per (chunk query tile, piece). A chunk sequence has at least 2 of
 // the num_tokens query rows and at most ceil(q_len / 256) <= q_len / 256 + 1
-// query tiles; the pieces add at most 2 * kPlanWGs / Hq per KV head (the
-// piece length is at least the chunk key tiles times Hq over 2 * kPlanWGs,
-// and an item of t tiles has at most t / length + 1 pieces).
+// query tiles; the pieces add at most kPlanWGs / Hq per KV head (the piece
+// length is at least the chunk key tiles times Hq over kPlanWGs, and an item
+// of t tiles has at most t / length + 1 pieces).
 inline int64_t plan_head_groups(int64_t num_seqs, int64_t num_tokens, int Hq, int Hkv,
                                 bool split) {
   const int64_t tiles = std::min(num_seqs, num_tokens / 2) + (num_tokens + 255) / 256;
-  const int64_t extra = split ? (2 * kPlanWGs + Hq - 1) / Hq : 0;
+  const int64_t extra = split ? (kPlanWGs + Hq - 1) / Hq : 0;
   return (int64_t)Hkv * (tiles + extra);
 }
 

@@ -795,7 +795,6 @@ __global__ __launch_bounds__(kPPW * 64, 1) void prefill_pp_kernel(PrefillArgs a,
 // at once.
 constexpr int kSortMax = 128;      // chunk sequences ordered by unit size, at most
 constexpr int kPlanThreads = 1024;
-constexpr int kChunkSplitFactor = 2;  // units per compute unit the split aims at
 
 // Key tiles of query tile qt of a chunk sequence (L keys, q_len queries
 // at the end, the query at position t seeing keys 0..t), as run_pp counts
@@ -805,12 +804,13 @@ __device__ __forceinline__ int chunk_item_tiles(int L, int q_len, int qt) {
   return (min(L, L - q_len + last_q) + BN - 1) / BN;
 }
 
-// Key tiles per piece the call aims at: all chunk items' key tiles (over
-// every query head) spread over kChunkSplitFactor units per workgroup of a
-// nominal grid of kPlanWGs (one per compute unit), never below
-// kChunkPieceTiles. Items already short enough stay whole, so a batch whose
-// chunk rows fill the chip by themselves is barely split. Computed by one
-// wave (lanes stride the sequences).
+// Key tiles per piece the call aims at: the chunk items' key tiles (over
+// every query head) shared out over kPlanWGs compute units, never below
+// kChunkPieceTiles. Only an item longer than that share is split, into the
+// fewest pieces no longer than it: a unit that outlasts a compute unit's fair
+// share sets the kernel's span, while splitting shorter ones only adds
+// partial results and their merge. Computed by one wave (lanes stride the
+// sequences).
 __device__ int chunk_piece_target(const PagedArgs& a) {
   const int lane = threadIdx.x & 63;
   long long tot = 0;
@@ -823,8 +823,7 @@ __device__ int chunk_piece_target(const PagedArgs& a) {
   }
 #pragma unroll
   for (int dd = 32; dd >= 1; dd >>= 1) tot += __shfl_xor(tot, dd);
-  const long long per_unit = (long long)kChunkSplitFactor * kPlanWGs;
-  return (int)max((long long)kChunkPieceTiles, (tot * a.Hq + per_unit - 1) / per_unit);
+  return (int)max((long long)kChunkPieceTiles, (tot * a.Hq + kPlanWGs - 1) / kPlanWGs);
 }
 
 // Pieces an item of `tiles` key tiles splits into at that target (1 when the
