@@ -142,3 +142,56 @@ def test_captured_prefill_replays_match_eager():
             ro, rl, rb = ref_prefill(qn, kn, vn, 1.0 / math.sqrt(d), causal=True, heads=[0, 5])
             assert_close(o_g[:, [0, 5]], ro[:, [0, 5]], torch.bfloat16, "graph prefill")
             assert_lse_close(lse_g[:, [0, 5]], rl[:, [0, 5]], rb[:, [0, 5]], "graph prefill lse")
+
+
+def test_captured_mixed_call_replays_match_eager_and_oracle():
+    # a paged call with chunk rows (one split along the keys) next to decodes:
+    # the planning, chunk, merge, split-KV decode and decode merge kernels all
+    # captured in one graph (the plan and partials live in the workspace and
+    # are rewritten by every replay). Three replays with new q contents and
+    # eager work in between; each equals the eager call bit for bit, the
+    # first also the oracle
+    print("[graph] mixed paged call, 3 replays", flush=True)
+    seq_lens = [6000, 40, 700, 3]
+    q_lens = [200, 1, 129, 1]
+    Hq, Hkv, d = 8, 2, 128
+    b = inputs.paged_inputs(len(seq_lens), Hq, Hkv, d, seq_lens=seq_lens, q_lens=q_lens, seed=95)
+    s = {k: v.to(DEV) for k, v in b.items() if torch.is_tensor(v)}
+    o = torch.empty_like(s["q"])
+    lse = torch.empty(s["q"].shape[0], Hq, device=DEV)
+    ws = torch.empty(attn.paged_workspace_size(len(seq_lens), sum(q_lens), Hq, Hkv, d,
+                                               b["max_seq_len"], b["max_query_len"]),
+                     dtype=torch.uint8, device=DEV)
+
+    def call():
+        attn.decode_paged(s["q"], s["k_cache"], s["v_cache"], s["block_table"], s["seq_lens"],
+                          max_seq_len=b["max_seq_len"], max_query_len=b["max_query_len"],
+                          query_start_loc=s["query_start_loc"], o=o, lse=lse, workspace=ws)
+
+    call()  # warm-up outside the capture (module load, first launch)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        q, _ = inputs.new_kv_rows(sum(q_lens), Hq, d, 500 + rep, device=DEV)
+        s["q"].copy_(q)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_g, lse_g = o.clone(), lse.clone()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        o.zero_()
+        lse.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o), f"replay {rep}: o differs from the eager call"
+        assert torch.equal(lse_g, lse), f"replay {rep}: lse differs from the eager call"
+        del junk
+        if rep == 0:
+            ro, rl, rb = ref_decode(s["q"].cpu(), b["k_cache"], b["v_cache"], b["block_table"],
+                                    b["seq_lens"], 1.0 / math.sqrt(d),
+                                    query_start_loc=b["query_start_loc"])
+            assert_close(o_g, ro, torch.bfloat16, "graph mixed call")
+            assert_lse_close(lse_g, rl, rb, "graph mixed call lse")
