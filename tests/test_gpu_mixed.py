@@ -103,7 +103,7 @@ def test_chunk_rows_match_contiguous_prefill():
 
 
 def test_mixed_many_sequences_direct_grid():
-    # more sequences than the persistent chunk kernel stages (2048): the chunk
+    # more sequences than the chunk planner handles (2048): the chunk
     # path then launches one workgroup per (query tile, sequence, head) of the
     # host bound, and workgroups of single-token sequences exit at once
     print("[mixed] 2100 sequences, chunks every 100th", flush=True)
@@ -126,10 +126,10 @@ def test_mixed_many_sequences_direct_grid():
 
 
 @pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 1)])
-def test_mixed_many_chunk_sequences_persistent_unsorted(d, Hq, Hkv):
-    # 200 chunk sequences (more than the 128 that the persistent chunk kernel
-    # orders by length) among 800 sequences (within the 2048 it stages): the
-    # persistent kernel then takes the chunk items in batch order. Chunks and
+def test_mixed_many_chunk_sequences_unsorted(d, Hq, Hkv):
+    # 200 chunk sequences (more than the 128 that the chunk planner orders by
+    # size) among 800 sequences (within the 2048 it plans): the plan then
+    # lists the chunk sequences in batch order. Chunks and
     # decodes interleave in the batch, chunks have ragged lengths and prior
     # context; every chunk and 40 decodes are checked against the oracle.
     print(f"[mixed] 800 sequences, 200 chunks, d={d}", flush=True)
@@ -150,6 +150,39 @@ def test_mixed_many_chunk_sequences_persistent_unsorted(d, Hq, Hkv):
     rows = torch.cat([torch.arange(int(qsl[m]), int(qsl[m + 1])) for m in seqs])
     assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "200 chunk sequences")
     assert_lse_close(lse[rows.to(DEV)], rl, rb, "200 chunk sequences")
+
+
+def test_many_chunk_sequences_unsorted_with_split_rows():
+    # 150 chunk sequences (more than the 128 the planner orders, so batch
+    # order) among 600, three of them after about 9000 cached tokens: those
+    # rows are split along the keys while the plan keeps batch order. Every
+    # chunk and 30 decodes are checked against the oracle.
+    print("[mixed] 600 sequences, 150 chunks, 3 split", flush=True)
+    rng = np.random.default_rng(77)
+    n = 600
+    chunk_ids = sorted(int(x) for x in rng.choice(n, 150, replace=False))
+    q_lens = [1] * n
+    for c in chunk_ids:
+        q_lens[c] = int(rng.integers(2, 65))
+    seq_lens = [q + int(rng.integers(0, 301)) for q in q_lens]
+    long_ids = chunk_ids[10::50]
+    for c in long_ids:
+        seq_lens[c] = q_lens[c] + 9000 + int(rng.integers(0, 200))
+    b = inputs.paged_inputs(n, 8, 2, 128, seq_lens=seq_lens, q_lens=q_lens, seed=77)
+    # room for key pieces only when some sequence may pass 4096 keys
+    assert attn.paged_workspace_size(n, sum(q_lens), 8, 2, 128, max(seq_lens), max(q_lens)) > \
+        attn.paged_workspace_size(n, sum(q_lens), 8, 2, 128, 4096, max(q_lens)) + \
+        attn.decode_paged_workspace_size(n, 8, 2, 128, max(seq_lens)) - \
+        attn.decode_paged_workspace_size(n, 8, 2, 128, 4096)
+    o, lse = run(b)
+    dec = sorted(set(int(x) for x in rng.choice(n, 50, replace=False)) - set(chunk_ids))[:30]
+    seqs = chunk_ids + dec
+    kc, vc, table, sl, q, qsl_c = inputs.compact_sequences(b, seqs)
+    ro, rl, rb = ref_decode(q, kc, vc, table, sl, 1.0 / math.sqrt(128), query_start_loc=qsl_c)
+    qsl = b["query_start_loc"]
+    rows = torch.cat([torch.arange(int(qsl[m]), int(qsl[m + 1])) for m in seqs])
+    assert_close(o[rows.to(DEV)], ro, torch.bfloat16, "150 chunk sequences, 3 split")
+    assert_lse_close(lse[rows.to(DEV)], rl, rb, "150 chunk sequences, 3 split")
 
 
 @pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 4, 1), (128, 16, 1), (64, 8, 8)])
