@@ -57,7 +57,7 @@ struct PagedArgs {
 };
 
 // Chunk rows are split along the keys in pieces of at least this many 64-key
-// tiles (4096 keys), by the persistent chunk kernel (batches of up to
+// tiles (4096 keys), by the planned chunk kernel (batches of up to
 // kPagedMaxSeqs sequences); the workspace holds ceil(max_seq_len / 4096)
 // pieces per row.
 constexpr int kChunkPieceTiles = 64;
