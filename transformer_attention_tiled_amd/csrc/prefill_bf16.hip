@@ -969,8 +969,9 @@ __global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(PagedArgs a) {
       if (r < m) first_of[r] = base + incl - cnt;
       base += __shfl(incl, 63);
     }
-    // the host's bound holds the list; the min only guards against seq_lens
-    // beyond the max_seq_len the workspace was sized for
+    // the host's bound holds the list of any batch within the documented
+    // preconditions; the min only keeps a batch outside them (query_start_loc
+    // past num_tokens, q_len past max_query_len) inside the workspace
     if (lane == 0) s_total = min(base, a.plan_cap);
   }
   __syncthreads();
